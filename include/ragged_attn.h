@@ -1,0 +1,157 @@
+/*
+ * ragged_attn.h -- C ABI of libragged_attn: ragged paged attention with the
+ * KV-cache update fused in, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (source: "Ragged Paged Attention: A High-Performance and
+ * Flexible LLM Inference Kernel for TPU", abstract; rocketrecap.com summary
+ * of the talk on that paper, points 00:01:30 "PagedAttention and
+ * mixed-batch problem" and 00:06:36 "kernel fusion of KV cache and
+ * attention", glossary entries "FlashAttention", "KV-Cache", "Mixed
+ * Batching", "PagedAttention", "Ragged Tensors"):
+ *
+ *   A batch holds R requests.  Request r brings q_r new tokens
+ *   (q_r = cu_q_lens[r+1] - cu_q_lens[r]; 1 for a decode step, more for a
+ *   prefill chunk, 0 allowed) on top of c_r = context_lens[r] tokens already
+ *   in the paged KV cache.  Its total length is L_r = c_r + q_r; position j
+ *   of the request lives in cache row (page_table[r][j / S], j % S).
+ *
+ *   1. KV-cache update: for every new token t and kv head h,
+ *        k_cache[slot_mapping[t] / S][slot_mapping[t] % S][h][:] = k_new[t][h][:]
+ *      and likewise for v.  A bit copy; no other cache row changes.
+ *   2. Attention: the i-th new token of request r (position c_r + i) and
+ *      q head h, reading kv head h / (Hq / Hkv), attends with exact softmax
+ *      attention over positions 0 .. c_r + i (causal, bottom-right aligned)
+ *      or 0 .. L_r - 1 (non-causal):
+ *        out[t][h][:] = sum_j softmax_j(scale * q[t][h] . K_j) V_j
+ *
+ * Layouts (row-major, no padding, bf16 = IEEE bfloat16 bit patterns):
+ *   q            [T][Hq][D]             bf16, device
+ *   k_new, v_new [T][Hkv][D]            bf16, device
+ *   k_cache,
+ *   v_cache      [P][S][Hkv][D]         bf16, device, updated in place
+ *   page_table   [R][max_pages_per_req] int32, device
+ *   cu_q_lens    [R + 1]                int32, device (and a host copy)
+ *   context_lens [R]                    int32, device (and a host copy)
+ *   slot_mapping [T]                    int32, device; must equal
+ *                page_table[r][(c_r+i)/S] * S + (c_r+i) % S for token i of r
+ *   out          [T][Hq][D]             bf16, device, written
+ *
+ * Supported: D in {64, 128, 256}; S = 16; Hq % Hkv == 0; Hq / Hkv <= 16.
+ *
+ * Ownership and concurrency: the caller owns every buffer, the workspace
+ * included; the library allocates no device memory and keeps no state
+ * between calls.  Host pointers are read during the call only.  ra_forward
+ * is asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
+ * never synchronises.  `out` must not alias any input.  A slot written by
+ * this call must not be read, as prior context, by any request of the same
+ * call.  Two calls that share a workspace must be ordered on one stream.
+ *
+ * Errors: every entry point returns a status and never aborts; the detail of
+ * the last failure on the calling thread is in ra_last_error().
+ */
+#ifndef RAGGED_ATTN_H
+#define RAGGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RA_OK = 0,
+    RA_E_NULL = 1,        /* a required pointer is NULL */
+    RA_E_SHAPE = 2,       /* sizes are inconsistent or negative */
+    RA_E_UNSUPPORTED = 3, /* valid, but outside what the library is built for */
+    RA_E_METADATA = 4,    /* metadata violates a precondition (ra_validate_metadata) */
+    RA_E_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
+    RA_E_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} ra_status;
+
+typedef struct {
+    int32_t num_reqs;          /* R >= 0 */
+    int32_t total_tokens;      /* T = cu_q_lens[R] */
+    int32_t num_q_heads;       /* Hq */
+    int32_t num_kv_heads;      /* Hkv, divides Hq */
+    int32_t head_dim;          /* D */
+    int32_t page_size;         /* S */
+    int32_t num_pages;         /* P, pages in k_cache / v_cache */
+    int32_t max_pages_per_req; /* columns of page_table */
+    float softmax_scale;       /* 0 means 1 / sqrt(D) */
+    int32_t causal;            /* nonzero: causal mask, bottom-right aligned */
+} ra_shape;
+
+/* Kernel variants.  RA_VARIANT_AUTO lets the dispatcher pick from the batch's
+ * decode/prefill mix (the distribution-aware dispatch of the paper's
+ * abstract, technique (3)); the others force one path for A/B runs. */
+typedef enum {
+    RA_VARIANT_AUTO = 0,
+    RA_VARIANT_GENERIC = 1,     /* one simple VALU kernel for every request */
+    RA_VARIANT_SPECIALISED = 2  /* decode kernel + MFMA prefill kernel */
+} ra_variant;
+
+/*
+ * Bytes of device workspace ra_forward needs for this batch (work list,
+ * split-KV partials).  Host copies of cu_q_lens [R+1] and context_lens [R]
+ * are read.  Returns 0 when the shape is invalid.  The size does not depend
+ * on the variant.
+ */
+size_t ra_workspace_bytes(const ra_shape *shape, const int32_t *cu_q_lens_host,
+                          const int32_t *context_lens_host);
+
+/*
+ * The fused call: KV-cache update plus attention, as defined above.
+ *
+ * cu_q_lens_host / context_lens_host: host copies of the device metadata;
+ * they must hold the same values (the dispatcher plans from them).
+ * workspace: device memory of at least ra_workspace_bytes() bytes, 256-byte
+ * aligned; its contents on entry do not matter.
+ * Checks are O(1) plus O(R) over the host metadata (cu_q_lens monotone and
+ * ending at T, c_r >= 0, L_r <= max_pages_per_req * S); the full
+ * O(T + pages) validation of page_table and slot_mapping is the separate
+ * ra_validate_metadata.  A call whose page_table or slot_mapping break the
+ * rules listed there is undefined.
+ * Returns RA_OK once the work is enqueued on `stream`.
+ */
+ra_status ra_forward(const ra_shape *shape,
+                     const void *q, const void *k_new, const void *v_new,
+                     void *k_cache, void *v_cache,
+                     const int32_t *page_table, const int32_t *cu_q_lens,
+                     const int32_t *context_lens, const int32_t *slot_mapping,
+                     const int32_t *cu_q_lens_host, const int32_t *context_lens_host,
+                     void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ra_forward with an explicit variant (RA_VARIANT_AUTO behaves as ra_forward). */
+ra_status ra_forward_variant(const ra_shape *shape,
+                             const void *q, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache,
+                             const int32_t *page_table, const int32_t *cu_q_lens,
+                             const int32_t *context_lens, const int32_t *slot_mapping,
+                             const int32_t *cu_q_lens_host, const int32_t *context_lens_host,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream,
+                             int32_t variant);
+
+/*
+ * Full metadata validation on host copies; touches no GPU.  Checks:
+ * cu_q_lens[0] == 0, non-decreasing, cu_q_lens[R] == T; c_r >= 0;
+ * L_r <= max_pages_per_req * S; the first ceil(L_r / S) page-table entries of
+ * every request lie in [0, P); slot_mapping agrees with the page table; no
+ * slot is written twice; Hq % Hkv == 0.  Returns RA_OK or RA_E_METADATA /
+ * RA_E_SHAPE / RA_E_NULL with the first failure in ra_last_error().
+ */
+ra_status ra_validate_metadata(const ra_shape *shape, const int32_t *page_table_host,
+                               const int32_t *cu_q_lens_host, const int32_t *context_lens_host,
+                               const int32_t *slot_mapping_host);
+
+/* Static description of a status code. */
+const char *ra_status_str(ra_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAGGED_ATTN_H */
