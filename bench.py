@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Throughput of the fused ragged paged attention call on one MI355X.
+
+One step = one ra_forward call over one batch (KV-cache update + attention
+for every request, with the plan, decode, prefill and merge kernels it
+needs), inputs resident in HBM.  Default workload: the Llama-3-8B-shaped
+decode batch (128 requests x 1 new token, contexts U[1024, 8192], Hq=32,
+Hkv=8, head_dim=128, page 16, bf16).  Prints ONE JSON line on stdout.
+
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--variant V]
+
+Roofline: the dominant kernel's algorithmic bytes (HBM-bound decode) or
+FLOPs (MFMA-bound prefill) per launch divided by its average launch time,
+measured with hipEvents the library records on its own stream around each
+stage.  The oracle (fp64 CPU) is timed on a bounded sample of the same
+workload as the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from ragged_paged_attention_amd import binding  # noqa: E402
+from ragged_paged_attention_amd.inputs import Batch, CONFIGS, config  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16
+
+WORKLOADS = {
+    "tiny": "tiny mixed batch: 2 decode (context 37, 100) + prefill 20 (context 0) + 33 (context 50), Hq=4 Hkv=2 D=64",
+    "decode": "decode: 128 requests x 1 new token, context U[1024,8192], Hq=32 Hkv=8 D=128, page 16, bf16",
+    "prefill": "prefill: 4 x 2048 new tokens, no context, causal, Hq=32 Hkv=8 D=128, page 16, bf16",
+    "prefill_noncausal": "prefill: 4 x 2048 new tokens, no context, non-causal, Hq=32 Hkv=8 D=128, page 16, bf16",
+    "mixed": "mixed: 96 decode (context U[512,8192]) + 8 x 512-token chunks (context U[0,4096]), shuffled, Hq=32 Hkv=8 D=128, page 16, bf16",
+    "decode_d256": "decode: 128 requests x 1 new token, context U[1024,4096], Hq=16 Hkv=8 D=256, page 16, bf16",
+    "prefill_d256": "prefill: 4 x 2048 new tokens, no context, causal, Hq=16 Hkv=8 D=256, page 16, bf16",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work (what the method must move / compute, nothing else)
+# ---------------------------------------------------------------------------
+def algorithmic_bytes(b: Batch, requests=None) -> int:
+    """Prior KV read + new KV read and written + q read + out written + page ids + metadata."""
+    cu = b.cu_q_lens.numpy().astype(np.int64)
+    ctx = b.context_lens.numpy().astype(np.int64)
+    rs = range(b.num_reqs) if requests is None else requests
+    Hq, Hkv, D, S = b.num_q_heads, b.num_kv_heads, b.head_dim, b.page_size
+    total = 0
+    for r in rs:
+        q = int(cu[r + 1] - cu[r])
+        c = int(ctx[r])
+        L = c + q
+        total += c * Hkv * D * 2 * 2          # prior K and V
+        total += q * Hkv * D * 2 * 2 * 2      # new K and V: read once, written once
+        total += q * Hq * D * 2 * 2           # q read, out written
+        total += 4 * ((L + S - 1) // S)       # page ids
+        total += 4 * (2 + q)                  # cu_q_lens, context_lens, slot_mapping
+    return total + 4
+
+
+def algorithmic_flops(b: Batch, requests=None) -> int:
+    """4*D FLOPs per visible (query, key) pair per q head (QK^T and PV)."""
+    cu = b.cu_q_lens.numpy().astype(np.int64)
+    ctx = b.context_lens.numpy().astype(np.int64)
+    rs = range(b.num_reqs) if requests is None else requests
+    pairs = 0
+    for r in rs:
+        q = int(cu[r + 1] - cu[r])
+        c = int(ctx[r])
+        if b.causal:
+            pairs += q * c + q * (q + 1) // 2
+        else:
+            pairs += q * (c + q)
+    return pairs * b.num_q_heads * 4 * b.head_dim
+
+
+def decode_requests(b: Batch):
+    ql = b.q_lens
+    return [r for r in range(b.num_reqs) if ql[r] == 1]
+
+
+def prefill_requests(b: Batch):
+    ql = b.q_lens
+    return [r for r in range(b.num_reqs) if ql[r] > 1]
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters, valid only for the kernel source they
+# were taken on.
+# ---------------------------------------------------------------------------
+def kernel_source_hash(stage: str) -> str:
+    name = {"decode": "decode.hip", "prefill": "prefill.hip"}[stage]
+    data = open(os.path.join(ROOT, "ragged_paged_attention_amd", "csrc", name), "rb").read()
+    return hashlib.sha256(data).hexdigest()[:16]
+
+
+def measured_traffic(stage: str, workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{workload}/{stage}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(stage):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+def sub_batch(b: Batch, reqs) -> Batch:
+    cu = b.cu_q_lens.tolist()
+    toks = [t for r in reqs for t in range(cu[r], cu[r + 1])]
+    qlens = [cu[r + 1] - cu[r] for r in reqs]
+    ncu = torch.tensor([0] + list(np.cumsum(qlens)), dtype=torch.int32)
+    idx = torch.tensor(toks, dtype=torch.int64)
+    return Batch(q=b.q[idx], k_new=b.k_new[idx], v_new=b.v_new[idx], k_cache=b.k_cache,
+                 v_cache=b.v_cache, page_table=b.page_table[list(reqs)], cu_q_lens=ncu,
+                 context_lens=b.context_lens[list(reqs)], slot_mapping=b.slot_mapping[idx],
+                 causal=b.causal, scale=b.scale)
+
+
+def cpu_baseline(b: Batch, kind: str, budget_s: float):
+    import oracle
+    from ragged_paged_attention_amd.inputs import u16
+
+    def run(reqs):
+        sb = sub_batch(b, reqs)
+        t = time.perf_counter()
+        oracle.forward(u16(sb.q), u16(sb.k_new), u16(sb.v_new), u16(sb.k_cache), u16(sb.v_cache),
+                       sb.page_table.numpy(), sb.cu_q_lens.numpy(), sb.context_lens.numpy(),
+                       sb.slot_mapping.numpy(), scale=b.effective_scale(), causal=b.causal)
+        return time.perf_counter() - t
+
+    order = list(range(b.num_reqs))
+    # probe with one request, then size the sample to the budget
+    t1 = run(order[:1])
+    n = int(max(1, min(len(order), budget_s / max(t1, 1e-3))))
+    reqs = order[:n]
+    secs = run(reqs)
+    toks = sum(b.q_lens[r] for r in reqs)
+    if kind == "hbm":
+        value, unit = algorithmic_bytes(b, reqs) / secs / 1e9, "GB/s"
+    else:
+        value, unit = algorithmic_flops(b, reqs) / secs / 1e12, "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {b.num_reqs} requests ({toks} new tokens), {secs:.1f} s "
+                      f"fp64, OpenMP over (token, q head)",
+            "tokens_per_s": toks / secs, "seconds": secs}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode", choices=[c for c in CONFIGS])
+    ap.add_argument("--variant", default="auto", choices=list(binding.VARIANTS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU-baseline budget (0 disables the oracle leg)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    log(f"[bench] building inputs for {args.config}")
+    b = config(args.config)
+    dev = torch.device("cuda:0")
+    dt = [t.to(dev) for t in (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
+                              b.cu_q_lens, b.context_lens, b.slot_mapping)]
+    call = binding.Prepared(*dt, causal=b.causal, scale=b.scale or None, variant=args.variant,
+                            cu_q_lens_host=b.cu_q_lens, context_lens_host=b.context_lens)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    log(f"[bench] R={b.num_reqs} T={b.total_tokens} pages={b.num_pages} "
+        f"workspace={call.workspace.numel()} B; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        call(stream)
+    torch.cuda.synchronize()
+
+    timers = [binding.StageTimer() for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        call(stream, timers[k])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    stages = {s: float(np.mean([t.stage_ms()[s] for t in timers])) for s in binding.STAGES}
+    for t in timers:
+        t.close()
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step; stages (us): "
+        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
+
+    B = algorithmic_bytes(b)
+    F = algorithmic_flops(b)
+    T = b.total_tokens
+    dec, pre = decode_requests(b), prefill_requests(b)
+    step_s = ms_per_step / 1e3
+    if args.variant == "generic":
+        dominant = "prefill"  # the generic kernel runs in the prefill stage slot
+        bound = "hbm" if not pre else "mfma"
+    else:
+        dominant = "decode" if stages["decode"] >= stages["prefill"] else "prefill"
+        bound = "hbm" if dominant == "decode" else "mfma"
+    kern_s = stages[dominant] / 1e3
+    if bound == "hbm":
+        units = algorithmic_bytes(b, dec if args.variant != "generic" else None)
+        achieved = units / kern_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": measured_traffic("decode", args.config) if dominant == "decode" else None,
+                "kernel": "decode_kernel" if args.variant != "generic" else "generic_kernel",
+                "algorithmic_bytes_per_launch": units, "kernel_us": kern_s * 1e6}
+    else:
+        units = algorithmic_flops(b, pre)
+        achieved = units / kern_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": measured_traffic("prefill", args.config),
+                "kernel": "prefill_kernel" if args.variant != "generic" else "generic_kernel",
+                "algorithmic_flops_per_launch": units, "kernel_us": kern_s * 1e6}
+
+    if pre and not dec:
+        metric, unit, value = "prefill TFLOP/s (% bf16 MFMA peak)", "TFLOP/s", F / step_s / 1e12
+        frac_step = value / MFMA_BF16_PEAK_TFLOPS
+    else:
+        metric, unit, value = "decode HBM GB/s (% of 8 TB/s)", "GB/s", B / step_s / 1e9
+        frac_step = value / HBM_PEAK_GBS
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] CPU baseline: oracle on a sample (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(b, "hbm" if unit == "GB/s" else "mfma", args.cpu_seconds)
+
+    line = {
+        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.config], "name": args.config,
+                   "requests": b.num_reqs, "total_tokens": T,
+                   "context_tokens": int(b.context_lens.sum()), "num_q_heads": b.num_q_heads,
+                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                   "page_size": b.page_size, "causal": b.causal, "variant": args.variant},
+        "tokens_per_s": T / step_s,
+        "frac_of_peak_whole_step": frac_step,
+        "algorithmic_bytes": B, "algorithmic_flops": F,
+        "stage_us": {k: v * 1e3 for k, v in stages.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "context": {"pages_decode_mbu_tpu7x": 0.86, "pages_prefill_mfu_tpu7x": 0.73,
+                    "pages_prefill_mfu_causal_tpu7x": 0.63},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

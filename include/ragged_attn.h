@@ -133,6 +133,24 @@ ra_status ra_forward_variant(const ra_shape *shape,
                              int32_t variant);
 
 /*
+ * ra_forward_variant that also records caller-created hipEvent_t handles on
+ * `stream` at the stage boundaries of the call, so that the caller can time
+ * each kernel: events[0] before the first launch, then events[1..4] after
+ * the plan, prefill, decode and merge stages, in that order (a stage that
+ * does not run still records its event, so its duration reads as ~0; the
+ * generic variant runs as the prefill stage).  n_events must be 5; events
+ * are not created, synchronised or destroyed by the library.
+ */
+ra_status ra_forward_profiled(const ra_shape *shape,
+                              const void *q, const void *k_new, const void *v_new,
+                              void *k_cache, void *v_cache,
+                              const int32_t *page_table, const int32_t *cu_q_lens,
+                              const int32_t *context_lens, const int32_t *slot_mapping,
+                              const int32_t *cu_q_lens_host, const int32_t *context_lens_host,
+                              void *out, void *workspace, size_t workspace_bytes, void *stream,
+                              int32_t variant, void *const *events, int32_t n_events);
+
+/*
  * Full metadata validation on host copies; touches no GPU.  Checks:
  * cu_q_lens[0] == 0, non-decreasing, cu_q_lens[R] == T; c_r >= 0;
  * L_r <= max_pages_per_req * S; the first ceil(L_r / S) page-table entries of

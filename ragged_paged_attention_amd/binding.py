@@ -61,6 +61,8 @@ def load_library():
     lib.ra_forward.argtypes = fwd_args
     lib.ra_forward_variant.restype = i32
     lib.ra_forward_variant.argtypes = fwd_args + [i32]
+    lib.ra_forward_profiled.restype = i32
+    lib.ra_forward_profiled.argtypes = fwd_args + [i32, P, i32]
     lib.ra_validate_metadata.restype = i32
     lib.ra_validate_metadata.argtypes = [shp, P, P, P, P]
     lib.ra_status_str.restype = ctypes.c_char_p
@@ -154,3 +156,79 @@ def forward(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_le
         ctypes.c_void_p(stream), VARIANTS[variant])
     _check(status)
     return out
+
+
+# --------------------------------------------------------------------------
+# Per-stage timing (plumbing for the bench: hipEvents through libamdhip64).
+# --------------------------------------------------------------------------
+STAGES = ("plan", "prefill", "decode", "merge")
+
+
+class StageTimer:
+    """Five hipEvents recorded by ra_forward_profiled at the stage boundaries."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = (ctypes.c_void_p * 5)()
+        for k in range(5):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events[k] = ev
+
+    def stage_ms(self) -> dict:
+        """Milliseconds of each stage of the last profiled call (waits for it)."""
+        if self.hip.hipEventSynchronize(self.events[4]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        out = {}
+        for k, name in enumerate(STAGES):
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[k], self.events[k + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = float(ms.value)
+        return out
+
+    def close(self):
+        for k in range(5):
+            if self.events[k]:
+                self.hip.hipEventDestroy(self.events[k])
+                self.events[k] = None
+
+
+class Prepared:
+    """A call with every argument marshalled once, for repeated launches.
+
+    Holds the shape, host copies, workspace and raw pointers, so that each
+    launch is one C call on the given stream.
+    """
+
+    def __init__(self, q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
+                 slot_mapping, *, causal=True, scale=None, out=None, variant="auto",
+                 cu_q_lens_host=None, context_lens_host=None):
+        self.lib = load_library()
+        self.shape = shape_of(q, k_cache, page_table, context_lens, scale=scale, causal=causal)
+        self.cu_h = _host_i32(cu_q_lens if cu_q_lens_host is None else cu_q_lens_host)
+        self.ctx_h = _host_i32(context_lens if context_lens_host is None else context_lens_host)
+        self.out = torch.empty_like(q) if out is None else out
+        nbytes = self.lib.ra_workspace_bytes(ctypes.byref(self.shape), _ptr(self.cu_h), _ptr(self.ctx_h))
+        self.workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=q.device)
+        self.variant = VARIANTS[variant]
+        self.keep = (q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
+                     slot_mapping)
+        self.args = [ctypes.byref(self.shape), *[_ptr(t) for t in self.keep], _ptr(self.cu_h),
+                     _ptr(self.ctx_h), _ptr(self.out), _ptr(self.workspace),
+                     ctypes.c_size_t(self.workspace.numel())]
+
+    def __call__(self, stream, timer: StageTimer | None = None):
+        if timer is None:
+            st = self.lib.ra_forward_variant(*self.args, ctypes.c_void_p(stream), self.variant)
+        else:
+            st = self.lib.ra_forward_profiled(*self.args, ctypes.c_void_p(stream), self.variant,
+                                              timer.events, 5)
+        _check(st)
+        return self.out

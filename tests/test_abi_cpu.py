@@ -1,0 +1,169 @@
+"""The C ABI without a GPU: the library loads, exports every symbol its header
+declares, and its host-side checks (shape, metadata, workspace) behave."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ragged_paged_attention_amd import binding
+from ragged_paged_attention_amd.inputs import config, random_batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ragged_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("ra_forward", "ra_forward_variant", "ra_forward_profiled", "ra_workspace_bytes",
+                 "ra_validate_metadata", "ra_status_str", "ra_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in ragged_attn.h but not exported"
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.ra_status_str(code).decode()
+        assert s.startswith(binding.STATUS[code])
+
+
+def shape_for(b, **over):
+    kw = dict(num_reqs=b.num_reqs, total_tokens=b.total_tokens, num_q_heads=b.num_q_heads,
+              num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, page_size=b.page_size,
+              num_pages=b.num_pages, max_pages_per_req=b.page_table.shape[1], causal=b.causal)
+    kw.update(over)
+    return binding.make_shape(**kw)
+
+
+def validate(b, shape=None, **over):
+    args = dict(page_table=b.page_table, cu_q_lens=b.cu_q_lens, context_lens=b.context_lens,
+                slot_mapping=b.slot_mapping)
+    args.update(over)
+    try:
+        binding.validate_metadata(shape or shape_for(b), **args)
+        return "RA_OK"
+    except binding.RaError as e:
+        return e.name
+
+
+def test_validate_accepts_generated_batches():
+    for b in [config("tiny")] + [random_batch(s, num_reqs=6, max_q=30, max_ctx=90, num_q_heads=8,
+                                              num_kv_heads=2, head_dim=64) for s in range(5)]:
+        assert validate(b) == "RA_OK"
+
+
+def test_validate_rejects_like_the_oracle():
+    """Each broken rule is rejected by the library and by the oracle's checker."""
+    b = config("tiny")
+    cases = []
+    cu = b.cu_q_lens.clone(); cu[0] = 1; cases.append(dict(cu_q_lens=cu))
+    ctx = b.context_lens.clone(); ctx[1] = -1; cases.append(dict(context_lens=ctx))
+    ctx = b.context_lens.clone(); ctx[0] = 5000; cases.append(dict(context_lens=ctx))
+    pt = b.page_table.clone(); pt[2, 0] = b.num_pages; cases.append(dict(page_table=pt))
+    pt = b.page_table.clone(); pt[3, 1] = -1; cases.append(dict(page_table=pt))
+    sm = b.slot_mapping.clone(); sm[4] += 1; cases.append(dict(slot_mapping=sm))
+    for over in cases:
+        got = validate(b, **over)
+        assert got == "RA_E_METADATA", over
+        args = dict(page_table=b.page_table, cu_q_lens=b.cu_q_lens, context_lens=b.context_lens,
+                    slot_mapping=b.slot_mapping)
+        args.update(over)
+        rc = oracle.check(*(args[k].numpy() for k in ("page_table", "cu_q_lens", "context_lens",
+                                                      "slot_mapping")),
+                          num_q_heads=b.num_q_heads, num_kv_heads=b.num_kv_heads,
+                          head_dim=b.head_dim, page_size=b.page_size, num_pages=b.num_pages)
+        assert rc != oracle.OK
+
+
+def test_validate_rejects_duplicate_slot():
+    # two decode requests whose new tokens land in the same slot
+    b = random_batch(3, num_reqs=2, max_q=1, max_ctx=20, num_q_heads=2, num_kv_heads=1,
+                     head_dim=64, decode_frac=1.0)
+    pt = b.page_table.clone()
+    ctx = b.context_lens.clone()
+    ctx[1] = ctx[0]
+    pt[1] = pt[0]
+    sm = b.slot_mapping.clone()
+    sm[1] = sm[0]
+    assert validate(b, page_table=pt, context_lens=ctx, slot_mapping=sm) == "RA_E_METADATA"
+    assert "twice" in binding.last_error()
+
+
+def test_shape_errors(lib):
+    b = config("tiny")
+    assert validate(b, shape=shape_for(b, num_q_heads=3)) == "RA_E_SHAPE"
+    assert validate(b, shape=shape_for(b, total_tokens=54)) == "RA_E_METADATA"
+    assert lib.ra_workspace_bytes(None, None, None) == 0
+
+
+def _forward_status(lib, shape, cu, ctx, ws_bytes=1 << 30, ptr=0x1000, ws_ptr=0x100000,
+                    variant=0):
+    """Call ra_forward_variant with fake device pointers (only host checks run)."""
+    P = ctypes.c_void_p
+    fake = P(ptr)
+    return lib.ra_forward_variant(ctypes.byref(shape), fake, fake, fake, fake, fake, fake, fake,
+                                  fake, fake, cu.data_ptr() and P(cu.data_ptr()),
+                                  P(ctx.data_ptr()), fake, P(ws_ptr), ctypes.c_size_t(ws_bytes),
+                                  None, variant)
+
+
+def test_forward_rejects_before_touching_the_gpu(lib):
+    b = config("tiny")
+    cu, ctx = b.cu_q_lens.clone(), b.context_lens.clone()
+    assert _forward_status(lib, shape_for(b, head_dim=96), cu, ctx) == 3  # unsupported
+    assert _forward_status(lib, shape_for(b, page_size=32), cu, ctx) == 3
+    assert _forward_status(lib, shape_for(b, num_kv_heads=3), cu, ctx) == 2
+    assert _forward_status(lib, shape_for(b), cu, ctx, ws_bytes=16) == 5  # workspace too small
+    assert _forward_status(lib, shape_for(b), cu, ctx, ws_ptr=0x100010) == 5  # misaligned
+    assert _forward_status(lib, shape_for(b), cu, ctx, variant=7) == 2
+    bad = cu.clone(); bad[2] = 0
+    assert _forward_status(lib, shape_for(b), bad, ctx) == 4
+    assert _forward_status(lib, shape_for(b, softmax_scale=-1.0) if False else
+                           shape_for(b, scale=float("inf")), cu, ctx) == 2
+
+
+def test_empty_batch_is_a_no_op(lib):
+    shape = binding.make_shape(num_reqs=0, total_tokens=0, num_q_heads=8, num_kv_heads=2,
+                               head_dim=128, page_size=16, num_pages=0, max_pages_per_req=0)
+    cu = torch.zeros(1, dtype=torch.int32)
+    ctx = torch.zeros(0, dtype=torch.int32)
+    st = lib.ra_forward_variant(ctypes.byref(shape), *([None] * 9), ctypes.c_void_p(cu.data_ptr()),
+                                ctypes.c_void_p(ctx.data_ptr() or 8), None, None,
+                                ctypes.c_size_t(0), None, 0)
+    assert st == 0, binding.last_error()
+
+
+def test_workspace_grows_with_split_requests(lib):
+    small = random_batch(5, num_reqs=4, max_q=1, max_ctx=100, num_q_heads=32, num_kv_heads=8,
+                         head_dim=128, decode_frac=1.0)
+    n_small = binding.workspace_bytes(shape_for(small), small.cu_q_lens, small.context_lens)
+    big = random_batch(5, num_reqs=4, max_q=1, max_ctx=5000, num_q_heads=32, num_kv_heads=8,
+                       head_dim=128, decode_frac=1.0)
+    n_big = binding.workspace_bytes(shape_for(big), big.cu_q_lens, big.context_lens)
+    assert n_small > 0 and n_big > n_small
+    assert n_small % 256 == 0 and n_big % 256 == 0

@@ -1,0 +1,234 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Bar: KV caches bit-exact over the whole tensors; attention output within
+max-abs 1e-2 of the oracle (bf16 I/O, fp32 accumulation); no NaN anywhere
+(unused cache slots hold the bf16 NaN sentinel, so a stray read shows up).
+Small batches are compared in full; the full-size workloads are compared on
+sampled (token, head) rows the oracle evaluates one by one, plus the full
+caches.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ragged_paged_attention_amd import binding
+from ragged_paged_attention_amd.inputs import Batch, build_batch, config, random_batch, u16
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+VARIANTS = ("generic", "specialised")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load_library()  # fail loudly when the library is not built
+    yield
+
+
+def run_gpu(b: Batch, variant="auto"):
+    dev = torch.device("cuda:0")
+    kc = b.k_cache.to(dev)
+    vc = b.v_cache.to(dev)
+    out = binding.forward(b.q.to(dev), b.k_new.to(dev), b.v_new.to(dev), kc, vc,
+                          b.page_table.to(dev), b.cu_q_lens.to(dev), b.context_lens.to(dev),
+                          b.slot_mapping.to(dev), causal=b.causal, scale=b.scale or None,
+                          cu_q_lens_host=b.cu_q_lens, context_lens_host=b.context_lens,
+                          variant=variant)
+    torch.cuda.synchronize()
+    return out.cpu(), kc.cpu(), vc.cpu()
+
+
+def oracle_full(b: Batch):
+    return oracle.forward(u16(b.q), u16(b.k_new), u16(b.v_new), u16(b.k_cache), u16(b.v_cache),
+                          b.page_table.numpy(), b.cu_q_lens.numpy(), b.context_lens.numpy(),
+                          b.slot_mapping.numpy(), scale=b.effective_scale(), causal=b.causal)
+
+
+def assert_close(out: torch.Tensor, ref: np.ndarray, what=""):
+    o = out.float().numpy()
+    assert not np.isnan(o).any(), f"{what}: NaN in output"
+    err = np.abs(o - ref)
+    worst = float(err.max(initial=0.0))
+    assert worst <= TOL, f"{what}: max abs error {worst:.3g} > {TOL}"
+    return worst
+
+
+def check_small(b: Batch, variant: str):
+    say(f"[parity] {b.name or 'batch'} variant={variant} R={b.num_reqs} T={b.total_tokens} "
+        f"Hq={b.num_q_heads} Hkv={b.num_kv_heads} D={b.head_dim} causal={b.causal}")
+    out, kc, vc = run_gpu(b, variant)
+    ref, rkc, rvc = oracle_full(b)
+    assert np.array_equal(u16(kc), rkc), "k_cache differs from the oracle's scatter"
+    assert np.array_equal(u16(vc), rvc), "v_cache differs from the oracle's scatter"
+    return assert_close(out, ref, b.name)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_tiny_workload(variant):
+    check_small(config("tiny"), variant)
+
+
+SMALL = [
+    # (seed, R, max_q, max_ctx, Hq, Hkv, D, decode_frac, causal)
+    (1, 6, 40, 90, 8, 2, 64, 0.5, True),
+    (2, 5, 70, 300, 32, 8, 128, 0.5, True),
+    (3, 4, 33, 200, 16, 8, 256, 0.5, True),
+    (4, 8, 1, 700, 32, 8, 128, 1.0, True),     # decode only, several splits
+    (5, 4, 150, 40, 32, 8, 128, 0.0, True),    # prefill only
+    (6, 5, 50, 60, 8, 8, 128, 0.5, True),      # G = 1
+    (7, 5, 50, 60, 16, 1, 64, 0.5, True),      # G = 16
+    (8, 4, 45, 80, 8, 1, 128, 0.5, True),      # G = 8
+    (9, 5, 60, 100, 12, 4, 128, 0.5, True),    # G = 3: generic fallback
+    (10, 5, 60, 100, 32, 8, 128, 0.3, False),  # non-causal
+    (11, 3, 20, 3000, 16, 4, 128, 0.7, True),  # long contexts
+    (12, 6, 90, 50, 4, 2, 256, 0.4, False),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"s{c[0]}")
+def test_random_batches(case, variant):
+    seed, R, mq, mc, Hq, Hkv, D, frac, causal = case
+    b = random_batch(seed, num_reqs=R, max_q=mq, max_ctx=mc, num_q_heads=Hq, num_kv_heads=Hkv,
+                     head_dim=D, decode_frac=frac, causal=causal)
+    check_small(b, variant)
+
+
+EDGES = {
+    # name: (q_lens, ctx_lens, Hq, Hkv, D)
+    "page_multiple": ([1, 1, 16], [15, 31, 16], 8, 2, 128),     # L = 16, 32, 32
+    "page_plus_one": ([1, 1, 17], [16, 32, 16], 8, 2, 128),     # L = 17, 33, 33
+    "fresh_decode": ([1, 1], [0, 0], 8, 2, 128),                # L = 1: out = v
+    "single_request": ([37], [100], 4, 2, 64),
+    "empty_requests": ([0, 3, 0, 1, 0], [5, 7, 0, 40, 0], 8, 2, 64),
+    "one_token_prefill_tail": ([129, 2, 1], [0, 1, 255], 8, 2, 128),
+    "long_decode_many_splits": ([1, 1, 1], [9000, 2500, 17], 32, 8, 128),
+    "d256_long": ([1, 70], [2100, 33], 16, 8, 256),
+}
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name", sorted(EDGES))
+def test_edge_cases(name, variant):
+    q, c, Hq, Hkv, D = EDGES[name]
+    b = build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, seed=sum(map(ord, name)),
+                    num_pages=sum((x + y + 15) // 16 for x, y in zip(q, c)) + 2, name=name)
+    check_small(b, variant)
+
+
+def test_fresh_decode_returns_v_new():
+    b = build_batch([1, 1], [0, 0], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=3)
+    out, _, _ = run_gpu(b)
+    want = b.v_new.repeat_interleave(4, dim=1)
+    assert torch.equal(out, want)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: whole caches bit-exact, sampled rows against the oracle.
+# ---------------------------------------------------------------------------
+def sample_rows(b: Batch, n, seed):
+    rng = np.random.default_rng(seed)
+    T, Hq = b.total_tokens, b.num_q_heads
+    cu = b.cu_q_lens.numpy()
+    toks = set()
+    for r in range(b.num_reqs):  # first and last token of every request
+        if cu[r + 1] > cu[r]:
+            toks.update([int(cu[r]), int(cu[r + 1] - 1)])
+    toks = sorted(toks)
+    extra = rng.integers(0, T, size=max(0, n - len(toks)))
+    tokens = np.array(list(toks) + list(extra), dtype=np.int32)
+    heads = rng.integers(0, Hq, size=len(tokens)).astype(np.int32)
+    return tokens, heads
+
+
+FULL = ("decode", "mixed", "prefill", "prefill_noncausal", "decode_d256", "prefill_d256")
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload(name):
+    say(f"[parity] full workload {name}: generating inputs")
+    b = config(name)
+    say(f"[parity] full workload {name}: R={b.num_reqs} T={b.total_tokens} P={b.num_pages}")
+    out, kc, vc = run_gpu(b)
+    say(f"[parity] full workload {name}: GPU done, checking")
+    S = b.page_size
+    rkc, rvc = oracle.scatter(u16(b.k_cache), u16(b.v_cache), u16(b.k_new), u16(b.v_new),
+                              b.slot_mapping.numpy(), page_size=S)
+    assert np.array_equal(u16(kc), rkc), "k_cache differs from the oracle's scatter"
+    assert np.array_equal(u16(vc), rvc), "v_cache differs from the oracle's scatter"
+    del kc, vc
+    o = out.float().numpy()
+    assert not np.isnan(o).any(), "NaN in output"
+    tokens, heads = sample_rows(b, 384, seed=7)
+    ref = oracle.attention_rows(u16(b.q), rkc, rvc, b.page_table.numpy(), b.cu_q_lens.numpy(),
+                                b.context_lens.numpy(), tokens, heads,
+                                scale=b.effective_scale(), causal=b.causal)
+    got = o[tokens, heads, :]
+    worst = float(np.abs(got - ref).max())
+    say(f"[parity] full workload {name}: max abs error {worst:.3g} over {len(tokens)} rows")
+    assert worst <= TOL
+
+
+# ---------------------------------------------------------------------------
+# Properties the HIP path must keep exactly.
+# ---------------------------------------------------------------------------
+def _mixed_small(seed=21):
+    return random_batch(seed, num_reqs=7, max_q=70, max_ctx=600, num_q_heads=32, num_kv_heads=8,
+                        head_dim=128, decode_frac=0.6)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_deterministic(variant):
+    b = _mixed_small()
+    o1, k1, _ = run_gpu(b, variant)
+    o2, k2, _ = run_gpu(b, variant)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+
+
+def test_page_permutation_invariance():
+    from tests.test_oracle import permute_pages
+    b = _mixed_small(22)
+    perm = np.random.default_rng(5).permutation(b.num_pages)
+    o1, _, _ = run_gpu(b)
+    o2, _, _ = run_gpu(permute_pages(b, perm))
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_request_order_invariance():
+    from tests.test_oracle import reorder_requests
+    b = _mixed_small(23)
+    order = np.random.default_rng(6).permutation(b.num_reqs)
+    nb, tok = reorder_requests(b, order)
+    o1, _, _ = run_gpu(b)
+    o2, _, _ = run_gpu(nb)
+    assert torch.equal(o1[torch.from_numpy(tok)].view(torch.int16), o2.view(torch.int16))
+
+
+def test_profiled_call_reports_stage_times():
+    b = _mixed_small(24)
+    dev = torch.device("cuda:0")
+    args = [t.to(dev) for t in (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
+                                b.cu_q_lens, b.context_lens, b.slot_mapping)]
+    call = binding.Prepared(*args, causal=b.causal, cu_q_lens_host=b.cu_q_lens,
+                            context_lens_host=b.context_lens)
+    timer = binding.StageTimer()
+    call(torch.cuda.current_stream().cuda_stream, timer)
+    ms = timer.stage_ms()
+    timer.close()
+    assert set(ms) == set(binding.STAGES)
+    assert all(v >= 0 for v in ms.values())
+    assert ms["decode"] > 0 and ms["prefill"] > 0
