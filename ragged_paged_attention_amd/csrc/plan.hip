@@ -21,6 +21,9 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 // every CU about three times over, a power of two between 256 and 1024
 // (the decode kernel holds one split's page ids in one VGPR: <= 64 pages).
 int choose_split(long long decode_keys, int Hkv, int S) {
+#ifdef RA_DECODE_SPLIT
+    if (RA_DECODE_SPLIT > 0) return RA_DECODE_SPLIT;
+#endif
     const long long target_waves = (long long)kNumCUs * kDecodeWavesPerCU * 3;
     long long c = (decode_keys * Hkv + target_waves - 1) / target_waves;
     long long p2 = 256;

@@ -59,6 +59,8 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
                        const StageEvents &ev);
 
 // Kernels of the specialised path.
+// kv heads per decode workgroup for this head_dim and kv-head count.
+int decode_heads_per_group(int D, int Hkv);
 hipError_t launch_decode(const Params &p, const Plan &plan, const int4 *items, float *part_o,
                          float *part_ml, hipStream_t stream);
 hipError_t launch_merge(const Params &p, const Plan &plan, const int4 *items, const float *part_o,
