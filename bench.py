@@ -2,8 +2,8 @@
 """Throughput of the fused ragged paged attention call on one MI355X.
 
 One step = one ra_forward call over one batch (KV-cache update + attention
-for every request, with the plan, decode, prefill and merge kernels it
-needs), inputs resident in HBM.  Default workload: the Llama-3-8B-shaped
+for every request, with the plan, prefill and decode kernels it needs),
+inputs resident in HBM.  Default workload: the Llama-3-8B-shaped
 decode batch (128 requests x 1 new token, contexts U[1024, 8192], Hq=32,
 Hkv=8, head_dim=128, page 16, bf16).  Prints ONE JSON line on stdout.
 

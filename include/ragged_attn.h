@@ -92,8 +92,9 @@ typedef enum {
 } ra_variant;
 
 /*
- * Bytes of device workspace ra_forward needs for this batch (work list,
- * split-KV partials).  Host copies of cu_q_lens [R+1] and context_lens [R]
+ * Bytes of device workspace ra_forward needs for this batch (work lists,
+ * merge counters and the partial results of decode requests that several
+ * workgroups share).  Host copies of cu_q_lens [R+1] and context_lens [R]
  * are read.  Returns 0 when the shape is invalid.  The size does not depend
  * on the variant.
  */
@@ -135,11 +136,11 @@ ra_status ra_forward_variant(const ra_shape *shape,
 /*
  * ra_forward_variant that also records caller-created hipEvent_t handles on
  * `stream` at the stage boundaries of the call, so that the caller can time
- * each kernel: events[0] before the first launch, then events[1..4] after
- * the plan, prefill, decode and merge stages, in that order (a stage that
- * does not run still records its event, so its duration reads as ~0; the
- * generic variant runs as the prefill stage).  n_events must be 5; events
- * are not created, synchronised or destroyed by the library.
+ * each kernel: events[0] before the first launch, then events[1..3] after
+ * the plan, prefill and decode stages, in that order (a stage that does not
+ * run still records its event, so its duration reads as ~0; the generic
+ * variant runs as the prefill stage).  n_events must be 4; events are not
+ * created, synchronised or destroyed by the library.
  */
 ra_status ra_forward_profiled(const ra_shape *shape,
                               const void *q, const void *k_new, const void *v_new,

@@ -1,11 +1,17 @@
 // decode.hip -- the HBM-bound decode kernel (requests with one new token).
 //
-// Work unit: one workgroup per (request r, key split [kb, ke), group of HW
-// kv heads), one wavefront per kv head; the G = Hq/Hkv query heads of a kv
-// head share every K/V byte its wavefront reads (grouped-query attention),
-// so the cache is read exactly once.
+// Work split (stream-K): the pages of all decode requests, in request order,
+// form one flat list; a persistent grid of workgroups per group of HW kv
+// heads takes equal consecutive ranges of it, so every compute unit streams
+// the same number of bytes however ragged the contexts are.  A workgroup
+// walks its range request by request ("segments"); a segment that is a whole
+// request writes the output, otherwise the workgroup writes a partial
+// (m, l, o) to a slot of its own, and a small merge kernel that follows
+// combines the partials of each such request by log-sum-exp.
 //
-// Per 16-token page:
+// One wavefront per kv head; the G = Hq/Hkv query heads of a kv head share
+// every K/V byte its wavefront reads (grouped-query attention), so the cache
+// is read exactly once.  Per 16-token page:
 //   * the workgroup loads the page's K and V blocks of its HW heads with
 //     16-byte loads in address order (each token row holds the HW heads
 //     side by side, so a page arrives as 16 contiguous segments of up to
@@ -17,17 +23,22 @@
 //     with Q^T (zero-padded to 16 heads) as B;
 //   * the S^T accumulator layout (lane = head, 4 keys per lane) is already
 //     the B-operand layout of v_mfma_f32_16x16x16_bf16 for O^T = V^T . P^T,
-//     so P never leaves its registers; V^T comes from the row-major V tile
+//     so P never leaves its registers (as a bf16 hi + lo pair, two MFMAs,
+//     keeping P to ~16 bits); V^T comes from the row-major V tile
 //     through the gfx950 transposing read ds_read_b64_tr_b16 (each 16-lane
 //     group points its lanes at 4 rows x 4 column quads, and lane j receives
 //     column j of the 4 rows);
 //   * the online softmax runs on S^T: per-head max across the 4 lane groups
 //     by two cross-lane steps, running sum kept per lane and reduced once;
 //     the accumulator is rescaled only when a max grows past a headroom.
-// The split that holds the new token's position writes its K/V rows into the
-// cache (the fused update); attention reads that key from k_new/v_new.
-// Splits of a request with more than one split write unnormalised partials
-// (o, m, l) that the merge kernel combines; single-split requests write out.
+// The workgroup that computes a request's last page writes the new token's
+// K/V rows into the cache (the fused update); attention reads that key from
+// k_new/v_new, so no workgroup reads a slot this launch writes.
+#include <stdlib.h>
+
+#include <algorithm>
+#include <type_traits>
+
 #include "launch.hpp"
 #include "plan.hpp"
 
@@ -38,10 +49,6 @@ namespace {
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
-
-// Orders this wavefront's LDS accesses (a workgroup is one wave, and the LDS
-// unit executes one wave's operations in order): a compiler-only fence.
-__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
 __device__ __forceinline__ short4_t lds_read_tr16(const bf16_t *p) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -54,11 +61,19 @@ __device__ __forceinline__ short4_t lds_read_tr16(const bf16_t *p) {
 #define RA_DECODE_PF64 3
 #endif
 #ifndef RA_DECODE_PF128
-#define RA_DECODE_PF128 3
+#define RA_DECODE_PF128 2
 #endif
 #ifndef RA_DECODE_PF256
-#define RA_DECODE_PF256 2
+#define RA_DECODE_PF256 1
 #endif
+
+// 1: P enters PV as a bf16 hi + lo pair (two MFMAs); 0: hi only.
+#ifndef RA_DECODE_P_LO
+#define RA_DECODE_P_LO 1
+#endif
+
+// Page ids a decode workgroup stages in LDS at a time.
+constexpr int kNumPids = 2048;
 
 // Headroom of the lazy softmax rescale, in log2 units.
 constexpr float kLazyLog2 = 8.f;
@@ -85,109 +100,180 @@ struct DecodeTile {
     short8_t v[NC];
 };
 
+// One request as the decode walk sees it.
+struct DecodeReq {
+    int i;     // index in the decode request list
+    int r;     // request id
+    int t0;    // its (single) token
+    int c;     // context length = position of the new token
+    int pfx;   // first flat page
+    int pend;  // one past its last flat page
+};
+
+// Metadata the kernel never writes, read through the constant address space:
+// with a uniform address the load is a scalar load, so the value lands in an
+// SGPR and waiting for it never waits for the K/V vector loads in flight.
+__device__ __forceinline__ int ld_meta(const int32_t *a, size_t i) {
+    return ((const __attribute__((address_space(4))) int32_t *)a)[i];
+}
+
+__device__ __forceinline__ DecodeReq fetch_req(const Params &p, const DecodeWork &dw, int i) {
+    DecodeReq q;
+    q.i = i;
+    q.r = ld_meta(dw.dreq, i);
+    q.pfx = ld_meta(dw.dpfx, i);
+    q.pend = ld_meta(dw.dpfx, i + 1);
+    q.t0 = ld_meta(p.cu_q_lens, q.r);
+    q.c = ld_meta(p.context_lens, q.r);
+    return q;
+}
+
+// Workgroup holding flat page g when NP pages are cut into nwg equal ranges
+// [floor(b NP / nwg), floor((b+1) NP / nwg)).
+__device__ __forceinline__ int wg_of_page(long long g, int np, int nwg) {
+    return (int)(((g + 1) * nwg + np - 1) / np) - 1;
+}
+
+// Partial slot of workgroup b for a request whose first page lies in
+// workgroup b_first: slot 1 of b when the request starts inside b's range
+// (it is b's last segment), else slot 0 (b's first segment).
+__device__ __forceinline__ int partial_slot(int hg, int b, int b_first, int nwg) {
+    return (hg * nwg + b) * 2 + (b == b_first ? 1 : 0);
+}
+
 template <int D, int HW, int PF>
-__global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, const int4 *__restrict__ items,
-                                                         float *__restrict__ part_o,
-                                                         float *__restrict__ part_ml) {
+__global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw) {
     using C = DecodeCfg<D, HW>;
     constexpr int KS = C::KS, MB = C::MB, CPH = C::CPH, CPR = C::CPR, NTHR = C::NTHR,
                   NC = C::NC, SWM = C::SWM, HEAD = C::HEAD, TENSOR = C::TENSOR,
                   STAGE = C::STAGE;
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    __shared__ int pid_lds[kNumPids];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n16 = lane & 15, kg = lane >> 4;
-    const int4 it = items[blockIdx.y];
-    const int r = it.x;
-    if (r < 0) return;
-    const int kb = it.y, ke = it.z, part = it.w;
+    const int hg = blockIdx.x, b = blockIdx.y;
+    const int np = dw.np, nwg = dw.nwg;
+    const int g0 = (int)(((long long)b * np) / nwg);
+    const int g1 = (int)(((long long)(b + 1) * np) / nwg);
+    if (g0 >= g1) return;
     const int Hkv = p.Hkv, G = p.Hq / Hkv;
-    const int hk0 = blockIdx.x * HW;  // first kv head of this workgroup
-    const int hk = hk0 + w;           // this wavefront's kv head
-    const int t0 = p.cu_q_lens[r];
-    const int c = p.context_lens[r];  // position of the new token; keys 0..c
-
-    // Fused KV-cache update of the new token (position c), heads hk0..hk0+HW-1.
-    if (c >= kb && c < ke) {
-        const size_t dst = ((size_t)p.slot_mapping[t0] * Hkv + hk0) * D;
-        const size_t src = ((size_t)t0 * Hkv + hk0) * D;
-        for (int ch = tid; ch < CPR; ch += NTHR) {
-            reinterpret_cast<uint4 *>(p.k_cache + dst)[ch] = reinterpret_cast<const uint4 *>(p.k_new + src)[ch];
-            reinterpret_cast<uint4 *>(p.v_cache + dst)[ch] = reinterpret_cast<const uint4 *>(p.v_new + src)[ch];
-        }
-    }
-
-    // Q^T as the B operand: lane (head n16, group kg) holds q[t0][hk*G + n16][32ks + 8kg .. +8].
-    short8_t qb[KS];
-    {
-        const bool hv = n16 < G;
-        const bf16_t *qrow = p.q + ((size_t)t0 * p.Hq + hk * G + (hv ? n16 : 0)) * D;
-        const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const short8_t x = *reinterpret_cast<const short8_t *>(qrow + 32 * ks + 8 * kg);
-            qb[ks] = hv ? x : z;
-        }
-    }
-
-    const int pg0 = kb >> 4, pg1 = (ke + 15) >> 4;  // <= 64 pages per split
-    const int32_t *ptab = p.page_table + (size_t)r * p.max_pages;
-    const int pid_vec = (pg0 + lane < pg1) ? ptab[pg0 + lane] : 0;
+    const int hk0 = hg * HW;   // first kv head of this workgroup
+    const int hk = hk0 + w;    // this wavefront's kv head
+    const size_t page_elems = (size_t)16 * Hkv * D;
 
     // Cooperative, contiguous page-block loads: chunk u of this thread is the
     // 16-byte chunk tid + NTHR*u of the page's HW-head row segments (row j,
     // head hh of the group, dim chunk dc); it lands in LDS at head hh, row j,
     // chunk dc ^ (j & SWM) (an XOR swizzle that keeps the MFMA-layout reads
     // below free of bank conflicts).
-    int row_u[NC], gofs_u[NC], lofs_u[NC], nofs_u[NC];
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-        const int q = tid + NTHR * u;
-        const int j = q / CPR, cc = q - j * CPR;
-        const int hh = cc / CPH, dc = cc - hh * CPH;
-        row_u[u] = j;
-        gofs_u[u] = (j * Hkv + hk0 + hh) * D + 8 * dc;
-        nofs_u[u] = (hk0 + hh) * D + 8 * dc;
-        lofs_u[u] = hh * HEAD + j * D + 8 * (dc ^ (j & SWM));
-    }
-    const size_t page_elems = (size_t)16 * Hkv * D;
-    const bf16_t *knew = p.k_new + (size_t)t0 * Hkv * D;
-    const bf16_t *vnew = p.v_new + (size_t)t0 * Hkv * D;
+    // Every chunk of a thread has the same head and dim chunk; its row
+    // advances by RPU = NTHR / CPR per chunk.
+    constexpr int RPU = NTHR / CPR;
+    static_assert(NTHR % CPR == 0, "a thread's chunks must share their column");
+    const int j0 = tid / CPR, cc = tid - j0 * CPR;
+    const int hh = cc / CPH, dc0 = cc - hh * CPH;
+    const int gofs0 = (j0 * Hkv + hk0 + hh) * D + 8 * dc0;  // + RPU*u rows of Hkv*D
+    const int nofs = (hk0 + hh) * D + 8 * dc0;
+    auto lds_ofs = [&](int u) {
+        const int j = j0 + RPU * u;
+        return hh * HEAD + j * D + 8 * (dc0 ^ (j & SWM));
+    };
 
-    auto load_page = [&](int pg, DecodeTile<NC> &tile) {
-        const size_t pid = (size_t)__builtin_amdgcn_readlane(pid_vec, pg - pg0);
+    // ---- page ids: the workgroup's flat pages, kNumPids at a time, go to
+    // LDS in one cooperative pass (a scalar walk over the requests they
+    // belong to), so that the page loop never waits on a memory round trip
+    // for an id --------------------------------------------------------------
+    const int first = ld_meta(dw.wstart, b);
+    DecodeReq fq = fetch_req(p, dw, first);  // fill cursor
+    int pid_base = g0;                       // flat page held in pid_lds[0]
+    auto fill_pids = [&]() {
+        const int ge = min(pid_base + kNumPids, g1);
+        while (pid_base >= fq.pend) fq = fetch_req(p, dw, fq.i + 1);
+        for (;;) {
+            const int sb = max(pid_base, fq.pfx), se = min(ge, fq.pend);
+            const int32_t *row = p.page_table + (size_t)fq.r * p.max_pages + (sb - fq.pfx);
+            for (int x = tid; x < se - sb; x += NTHR) pid_lds[sb - pid_base + x] = row[x];
+            if (fq.pend >= ge) break;
+            fq = fetch_req(p, dw, fq.i + 1);
+        }
+        __syncthreads();
+    };
+    fill_pids();
+
+    // ---- load cursor: walks the flat pages g0.. in order, PF ahead ---------
+    DecodeReq lq = fetch_req(p, dw, first);
+    // Pages past the workgroup's range (the ring's last PF loads) read the
+    // new-token rows of the current request instead: the instruction stream
+    // stays the same on every path, so the compiler's wait counts stay exact
+    // (a path without the prefetch would make it wait for every load), and
+    // those few rows are cache hits.
+    auto load_page = [&](int g, DecodeTile<NC> &tile) {
+        const bool real = g < g1;
+        size_t pid = 0;
+        int pr = 0;
+        if (real) {
+            if (g - pid_base >= kNumPids) {  // next batch of ids (all waves are here)
+                __syncthreads();
+                pid_base += kNumPids;
+                fill_pids();
+            }
+            while (g >= lq.pend) lq = fetch_req(p, dw, lq.i + 1);
+            pr = g - lq.pfx;  // page index inside the request
+            pid = (size_t)__builtin_amdgcn_readfirstlane(pid_lds[g - pid_base]);
+        }
+        const bf16_t *knew = p.k_new + (size_t)lq.t0 * Hkv * D;
+        const bf16_t *vnew = p.v_new + (size_t)lq.t0 * Hkv * D;
 #pragma unroll
         for (int u = 0; u < NC; ++u) {
             // Positions >= c are the new token (read from k_new / v_new: the
             // same bits, and never the slot this launch writes) or lie past
             // the request (their scores are masked; reading the new row keeps
             // the stand-in V finite, so 0 * V stays 0).
-            const bool cached = pg * 16 + row_u[u] < c;
-            const bf16_t *ks = cached ? p.k_cache + pid * page_elems + gofs_u[u] : knew + nofs_u[u];
-            const bf16_t *vs = cached ? p.v_cache + pid * page_elems + gofs_u[u] : vnew + nofs_u[u];
-            tile.k[u] = *reinterpret_cast<const short8_t *>(ks);
-            tile.v[u] = *reinterpret_cast<const short8_t *>(vs);
+            const bool cached = real && pr * 16 + j0 + RPU * u < lq.c;
+            const int gofs = gofs0 + RPU * u * Hkv * D;
+            const bf16_t *ksrc = cached ? p.k_cache + pid * page_elems + gofs : knew + nofs;
+            const bf16_t *vsrc = cached ? p.v_cache + pid * page_elems + gofs : vnew + nofs;
+            tile.k[u] = *reinterpret_cast<const short8_t *>(ksrc);
+            tile.v[u] = *reinterpret_cast<const short8_t *>(vsrc);
         }
     };
     auto store_page = [&](int stage, const DecodeTile<NC> &tile) {
         bf16_t *kbase = smem + stage * STAGE;
 #pragma unroll
         for (int u = 0; u < NC; ++u) {
-            *reinterpret_cast<short8_t *>(kbase + lofs_u[u]) = tile.k[u];
-            *reinterpret_cast<short8_t *>(kbase + TENSOR + lofs_u[u]) = tile.v[u];
+            const int lo = lds_ofs(u);
+            *reinterpret_cast<short8_t *>(kbase + lo) = tile.k[u];
+            *reinterpret_cast<short8_t *>(kbase + TENSOR + lo) = tile.v[u];
         }
     };
+
+    // ---- compute cursor: the request being accumulated ---------------------
+    DecodeReq cq = lq;
+    int seg_g = g0;  // first flat page of the current segment
+    short8_t qb[KS];
+    // Q^T as the B operand: lane (head n16, group kg) holds q[t0][hk*G + n16][32ks + 8kg .. +8].
+    auto load_q = [&]() {
+        const bool hv = n16 < G;
+        const bf16_t *qrow = p.q + ((size_t)cq.t0 * p.Hq + hk * G + (hv ? n16 : 0)) * D;
+        const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const short8_t x = *reinterpret_cast<const short8_t *>(qrow + 32 * ks + 8 * kg);
+            qb[ks] = hv ? x : z;
+        }
+    };
+    load_q();
 
     float4_t o[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) o[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = p.scale_log2;
-    const int kend = min(ke, c + 1);
-    // This lane's K row (A operand) and V^T transposing-read row.
+    // This lane's V^T transposing-read row.
     const int vrow = 4 * kg + (n16 >> 2);
 
-    auto compute_page = [&](int pg, int stage) {
+    auto compute_page = [&](int pr, int stage) {
         const bf16_t *kt = smem + stage * STAGE + w * HEAD;
         const bf16_t *vt = kt + TENSOR;
         // S^T[key][head] = K . Q^T for the 16 keys of this page.
@@ -198,11 +284,12 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, const int4 *_
             const short8_t a = *reinterpret_cast<const short8_t *>(kt + n16 * D + 8 * (dc ^ (n16 & SWM)));
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s, 0, 0, 0);
         }
-        // Online softmax; this lane holds keys pg*16 + 4kg + i of head n16.
-        const int jb = pg * 16 + 4 * kg;
+        // Online softmax; this lane holds keys pr*16 + 4kg + i of head n16,
+        // visible when <= c.
+        const int jb = pr * 16 + 4 * kg;
         float sc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = (jb + i < kend) ? s[i] * sl2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) sc[i] = (jb + i <= cq.c) ? s[i] * sl2 : -INFINITY;
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -217,17 +304,25 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, const int4 *_
             for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
             m_run = mn;
         }
-        float pr[4];
+        float pr4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - m_run);
-        l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        const uint32_t p01 = cvt_pk_bf16(pr[0], pr[1]);
-        const uint32_t p23 = cvt_pk_bf16(pr[2], pr[3]);
-        short4_t pb;
-        pb[0] = (short)(p01 & 0xffff);
-        pb[1] = (short)(p01 >> 16);
-        pb[2] = (short)(p23 & 0xffff);
-        pb[3] = (short)(p23 >> 16);
+        for (int i = 0; i < 4; ++i) pr4[i] = fast_exp2(sc[i] - m_run);
+        l_run += (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
+        // P as a bf16 pair hi + lo (lo = the rounding residue of hi), so the
+        // PV product keeps ~16 bits of P: the MFMA work is negligible next to
+        // the page's HBM time, and the only rounding left is the output's.
+        short4_t pb_hi, pb_lo;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            const uint32_t hi = cvt_pk_bf16(pr4[i], pr4[i + 1]);
+            const float r0 = pr4[i] - __uint_as_float(hi << 16);
+            const float r1 = pr4[i + 1] - __uint_as_float(hi & 0xffff0000u);
+            const uint32_t lo = cvt_pk_bf16(r0, r1);
+            pb_hi[i] = (short)(hi & 0xffff);
+            pb_hi[i + 1] = (short)(hi >> 16);
+            pb_lo[i] = (short)(lo & 0xffff);
+            pb_lo[i + 1] = (short)(lo >> 16);
+        }
         // O^T[d][head] += V^T[d][key] . P^T[key][head]; A = V^T by transposing
         // reads: lane reads row vrow, columns 16mb + 4(n16 & 3) .. +4.
 #pragma unroll
@@ -235,88 +330,221 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, const int4 *_
             const int e = 16 * mb + 4 * (n16 & 3);
             const int dc = e >> 3;
             const short4_t va = lds_read_tr16(vt + vrow * D + 8 * (dc ^ (vrow & SWM)) + (e & 7));
-            o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[mb], 0, 0, 0);
+            o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_hi, o[mb], 0, 0, 0);
+#if RA_DECODE_P_LO
+            o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb_lo, o[mb], 0, 0, 0);
+#endif
         }
     };
 
-    // Ring of PF + 1 page tiles in registers: pages pg+1 .. pg+PF are in
-    // flight while page pg goes to LDS stage pg & 1 and is computed.  One
-    // barrier per page: a stage is rewritten two pages later, after every
-    // wavefront has passed the barrier that follows its last read.
-    constexpr int NR = PF + 1;
-    DecodeTile<NC> ring[NR];
+    // End of a segment (the part of request cq inside this workgroup): write
+    // the output when the segment is the whole request, otherwise a partial;
+    // the last workgroup of the request to finish merges the partials.
+    auto finish_segment = [&](int g_last) {
+        float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+        l_tot += __shfl_xor(l_tot, 32, 64);
+        const int b_first = wg_of_page(cq.pfx, np, nwg);
+        const int b_last = wg_of_page(cq.pend - 1, np, nwg);
+        const bool hv = n16 < G;
+        const int h = hk * G + n16;  // q head
+        bf16_t *orow = p.out + ((size_t)cq.t0 * p.Hq + h) * D;
+        if (b_first == b_last) {
+            if (hv) {
+                const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int k = 0; k < PF; ++k)
-        if (pg0 + k < pg1) load_page(pg0 + k, ring[k]);
-    for (int pg = pg0; pg < pg1; pg += NR) {
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            if (pg + k >= pg1) break;
-            if (pg + k + PF < pg1) load_page(pg + k + PF, ring[(k + PF) % NR]);
-            store_page((pg + k) & 1, ring[k]);
-            __syncthreads();
-            compute_page(pg + k, (pg + k) & 1);
-        }
-    }
-
-    // Row sums: add the four lane groups of each head.
-    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-
-    if (n16 < G) {
-        const int h = hk * G + n16;
-        if (part < 0) {
-            const float inv = 1.f / l_tot;
-            bf16_t *orow = p.out + ((size_t)t0 * p.Hq + h) * D;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                uint2 wv;
-                wv.x = cvt_pk_bf16(o[mb][0] * inv, o[mb][1] * inv);
-                wv.y = cvt_pk_bf16(o[mb][2] * inv, o[mb][3] * inv);
-                *reinterpret_cast<uint2 *>(orow + 16 * mb + 4 * kg) = wv;
+                for (int mb = 0; mb < MB; ++mb) {
+                    uint2 wv;
+                    wv.x = cvt_pk_bf16(o[mb][0] * inv, o[mb][1] * inv);
+                    wv.y = cvt_pk_bf16(o[mb][2] * inv, o[mb][3] * inv);
+                    *reinterpret_cast<uint2 *>(orow + 16 * mb + 4 * kg) = wv;
+                }
             }
-        } else {
-            float *prow = part_o + ((size_t)part * p.Hq + h) * D;
+            return;
+        }
+        // Partial slot: a workgroup's last segment (the request starts inside
+        // its range) uses slot 1, its first segment slot 0.  The merge kernel
+        // combines the slots of the request's workgroups after this launch
+        // (a kernel boundary makes them visible without device-wide fences,
+        // which flush the L2 of every XCD and would stall the streaming).
+        if (hv) {
+            const size_t sidx = (size_t)partial_slot(hg, b, b_first, nwg) * (HW * G) + w * G + n16;
+            float *prow = dw.part_o + sidx * D;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 *reinterpret_cast<float4_t *>(prow + 16 * mb + 4 * kg) = o[mb];
             if (kg == 0) {
-                part_ml[((size_t)part * p.Hq + h) * 2] = m_run;
-                part_ml[((size_t)part * p.Hq + h) * 2 + 1] = l_tot;
+                dw.part_ml[sidx * 2] = m_run;
+                dw.part_ml[sidx * 2 + 1] = l_tot;
             }
         }
+        (void)g_last;
+    };
+
+    // One flat page through the pipeline: fused KV update on the request's
+    // last page, scores/softmax/PV, and the end of the segment.
+    auto step = [&](int g, int stage) {
+        const int pr = g - cq.pfx;
+        if (g == cq.pend - 1 && lane < CPH) {
+            // Fused KV-cache update of the new token (position c), this
+            // wavefront's kv head: the row is in the LDS tile already (loaded
+            // from k_new / v_new), so the copy waits on no global load.
+            const int j = cq.c & 15, dc = lane;
+            const bf16_t *kt = smem + stage * STAGE + w * HEAD + j * D + 8 * (dc ^ (j & SWM));
+            const short8_t kr = *reinterpret_cast<const short8_t *>(kt);
+            const short8_t vr = *reinterpret_cast<const short8_t *>(kt + TENSOR);
+            const size_t dst = ((size_t)ld_meta(p.slot_mapping, cq.t0) * Hkv + hk) * D + 8 * dc;
+            *reinterpret_cast<short8_t *>(p.k_cache + dst) = kr;
+            *reinterpret_cast<short8_t *>(p.v_cache + dst) = vr;
+        }
+        compute_page(pr, stage);
+        if (g == cq.pend - 1 || g == g1 - 1) {
+            finish_segment(g);
+            if (g + 1 < g1) {
+                cq = fetch_req(p, dw, cq.i + 1);
+                seg_g = g + 1;
+                load_q();
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) o[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+                m_run = -INFINITY;
+                l_run = 0.f;
+            }
+        }
+    };
+
+    // Ring of PF + 1 page tiles in registers: pages g+1 .. g+PF are in flight
+    // while page g goes to LDS stage g & 1 and is computed.  One barrier per
+    // page: a stage is rewritten two pages later, after every wavefront has
+    // passed the barrier that follows its last read.
+    constexpr int NR = PF + 1;
+    DecodeTile<NC> ring[NR];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) load_page(g0 + k, ring[k]);
+    for (int g = g0; g < g1; g += NR) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            if (g + k >= g1) break;
+            load_page(g + k + PF, ring[(k + PF) % NR]);
+            store_page((g + k) & 1, ring[k]);
+            __syncthreads();
+            step(g + k, (g + k) & 1);
+        }
+    }
+    (void)seg_g;
+}
+
+// Log-sum-exp merge of the partials of every decode request that several
+// workgroups share: one workgroup per (head group, request), one wavefront
+// per kv head, lanes laid out like the decode accumulators.
+//   M = max_s m_s,  out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+// (m is kept in the exp2 domain).
+template <int D, int HW>
+__global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeWork dw) {
+    constexpr int MB = D / 16;
+    const int hg = blockIdx.x, i = blockIdx.y;
+    const int pfx = ld_meta(dw.dpfx, i), pend = ld_meta(dw.dpfx, i + 1);
+    const int b_first = wg_of_page(pfx, dw.np, dw.nwg);
+    const int b_last = wg_of_page(pend - 1, dw.np, dw.nwg);
+    if (b_first == b_last) return;  // written by the decode kernel
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n16 = lane & 15, kg = lane >> 4;
+    const int G = p.Hq / p.Hkv;
+    if (n16 >= G) return;
+    const int hl = w * G + n16;  // q head inside the head group
+    const int r = ld_meta(dw.dreq, i);
+    const int t0 = ld_meta(p.cu_q_lens, r);
+    float M = -INFINITY;
+    for (int bb = b_first; bb <= b_last; ++bb)
+        M = fmaxf(M, dw.part_ml[((size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl) * 2]);
+    float4_t acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int bb = b_first; bb <= b_last; ++bb) {
+        const size_t sidx = (size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl;
+        const float wgt = fast_exp2(dw.part_ml[sidx * 2] - M);
+        den += wgt * dw.part_ml[sidx * 2 + 1];
+        const float *prow = dw.part_o + sidx * D;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            acc[mb] += wgt * *reinterpret_cast<const float4_t *>(prow + 16 * mb + 4 * kg);
+    }
+    const float inv = 1.f / den;
+    bf16_t *orow = p.out + ((size_t)t0 * p.Hq + (hg * HW + w) * G + n16) * D;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        uint2 wv;
+        wv.x = cvt_pk_bf16(acc[mb][0] * inv, acc[mb][1] * inv);
+        wv.y = cvt_pk_bf16(acc[mb][2] * inv, acc[mb][3] * inv);
+        *reinterpret_cast<uint2 *>(orow + 16 * mb + 4 * kg) = wv;
     }
 }
 
 template <int D, int HW, int PF>
-hipError_t launch_decode_cfg(const Params &p, const Plan &plan, const int4 *items, float *part_o,
-                             float *part_ml, hipStream_t stream) {
-    using C = DecodeCfg<D, HW>;
+hipError_t configure_decode() {
     static bool configured = false;
     if (!configured) {
         hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<D, HW, PF>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)C::LDS_BYTES);
+                                           (int)DecodeCfg<D, HW>::LDS_BYTES);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    dim3 grid(p.Hkv / HW, plan.n_decode_items);
-    hipLaunchKernelGGL((decode_kernel<D, HW, PF>), grid, dim3(64 * HW), C::LDS_BYTES, stream, p,
-                       items, part_o, part_ml);
+    return hipSuccess;
+}
+
+// Workgroups of this configuration resident at once on the whole device.
+template <int D, int HW, int PF>
+hipError_t decode_capacity(int *cap) {
+    hipError_t e = configure_decode<D, HW, PF>();
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 0, per_cu = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, HW, PF>, 64 * HW,
+                                                         DecodeCfg<D, HW>::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    *cap = std::max(1, cus * std::max(1, per_cu));
+    return hipSuccess;
+}
+
+template <int D, int HW, int PF>
+hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t stream) {
+    hipError_t e = configure_decode<D, HW, PF>();
+    if (e != hipSuccess) return e;
+    const dim3 grid(p.Hkv / HW, dw.nwg);
+    const size_t lds = DecodeCfg<D, HW>::LDS_BYTES;
+    hipLaunchKernelGGL((decode_kernel<D, HW, PF>), grid, dim3(64 * HW), lds, stream, p, dw);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid(p.Hkv / HW, dw.nd);
+    hipLaunchKernelGGL((decode_merge_kernel<D, HW>), mgrid, dim3(64 * HW), 0, stream, p, dw);
     return hipGetLastError();
 }
 
-template <int D, int PF>
-hipError_t launch_decode_d(const Params &p, const Plan &plan, const int4 *items, float *part_o,
-                           float *part_ml, hipStream_t stream) {
-    switch (decode_heads_per_group(D, p.Hkv)) {
-        case 8: if constexpr (D <= 128) return launch_decode_cfg<D, 8, PF>(p, plan, items, part_o, part_ml, stream); break;
-        case 4: return launch_decode_cfg<D, 4, PF>(p, plan, items, part_o, part_ml, stream);
-        case 2: return launch_decode_cfg<D, 2, PF>(p, plan, items, part_o, part_ml, stream);
-        case 1: return launch_decode_cfg<D, 1, PF>(p, plan, items, part_o, part_ml, stream);
+// Calls f.template operator()<HW>() with the compile-time head-group size.
+template <int D, int PF, typename F>
+hipError_t with_hw(int Hkv, F &&f) {
+    switch (decode_heads_per_group(D, Hkv)) {
+        case 8: if constexpr (D <= 128) return f(std::integral_constant<int, 8>()); break;
+        case 4: return f(std::integral_constant<int, 4>());
+        case 2: return f(std::integral_constant<int, 2>());
+        case 1: return f(std::integral_constant<int, 1>());
         default: break;
     }
     return hipErrorInvalidValue;
+}
+
+template <int D, int PF>
+hipError_t launch_decode_d(const Params &p, const DecodeWork &dw, hipStream_t stream) {
+    return with_hw<D, PF>(p.Hkv, [&](auto hw) {
+        return launch_decode_cfg<D, decltype(hw)::value, PF>(p, dw, stream);
+    });
+}
+
+template <int D, int PF>
+hipError_t capacity_d(int Hkv, int *cap) {
+    return with_hw<D, PF>(Hkv, [&](auto hw) { return decode_capacity<D, decltype(hw)::value, PF>(cap); });
 }
 
 }  // namespace
@@ -330,12 +558,34 @@ int decode_heads_per_group(int D, int Hkv) {
     return 1;
 }
 
-hipError_t launch_decode(const Params &p, const Plan &plan, const int4 *items, float *part_o,
-                         float *part_ml, hipStream_t stream) {
+hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg) {
+    int cap = 0;
+    hipError_t e;
     switch (p.D) {
-        case 64: return launch_decode_d<64, RA_DECODE_PF64>(p, plan, items, part_o, part_ml, stream);
-        case 128: return launch_decode_d<128, RA_DECODE_PF128>(p, plan, items, part_o, part_ml, stream);
-        case 256: return launch_decode_d<256, RA_DECODE_PF256>(p, plan, items, part_o, part_ml, stream);
+        case 64: e = capacity_d<64, RA_DECODE_PF64>(p.Hkv, &cap); break;
+        case 128: e = capacity_d<128, RA_DECODE_PF128>(p.Hkv, &cap); break;
+        case 256: e = capacity_d<256, RA_DECODE_PF256>(p.Hkv, &cap); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    // One resident wave of workgroups, none with fewer than kMinPages pages.
+    // RA_DECODE_WGS (environment) overrides the resident count, for tuning.
+    constexpr int kMinPages = 4;
+    const char *env = getenv("RA_DECODE_WGS");
+    const int forced = env ? atoi(env) : 0;
+    if (forced > 0) cap = forced * plan.decode_hgroups;
+    int n = std::max(1, cap / plan.decode_hgroups);
+    n = std::min(n, plan.decode_wg_cap);
+    n = std::min(n, std::max(1, plan.n_decode_pages / kMinPages));
+    *nwg = n;
+    return hipSuccess;
+}
+
+hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream) {
+    switch (p.D) {
+        case 64: return launch_decode_d<64, RA_DECODE_PF64>(p, dw, stream);
+        case 128: return launch_decode_d<128, RA_DECODE_PF128>(p, dw, stream);
+        case 256: return launch_decode_d<256, RA_DECODE_PF256>(p, dw, stream);
         default: return hipErrorInvalidValue;
     }
 }

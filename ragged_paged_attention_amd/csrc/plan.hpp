@@ -1,16 +1,23 @@
 // plan.hpp -- the distribution-aware dispatcher: how a batch is cut into
-// work items and which kernels run (internal to the library).
+// work and which kernels run (internal to the library).
 //
 // The batch is classified per request from the host copies of cu_q_lens and
 // context_lens: q_r == 1 is a decode request, q_r > 1 a prefill chunk,
-// q_r == 0 has nothing to do.  Decode requests are cut along the key axis
-// into splits of `split_tokens` keys (flash-decoding style), so that short
-// and long contexts alike spread over all compute units; requests with more
-// than one split get a log-sum-exp merge.  Prefill chunks are cut into query
-// tiles of `q_tile` tokens per kv head.  The host computes only the counts
-// and the workspace layout; a one-workgroup plan kernel writes the item
-// lists from the device copies of the same metadata, so no host-to-device
-// copy is needed.
+// q_r == 0 has nothing to do.
+//
+// Decode: the pages of all decode requests, in request order, form one flat
+// list of NP pages; a persistent grid of NW workgroups per kv-head group
+// takes NP / NW consecutive pages each (stream-K style), so every compute
+// unit streams the same number of bytes whatever the context lengths.  A
+// request cut by a workgroup boundary is finished by a merge kernel that
+// log-sum-exp combines the partial (m, l, o) of its workgroups.
+//
+// Prefill: chunks are cut into query tiles of `q_tile` tokens per kv head.
+//
+// The host computes counts and the workspace layout only; a one-workgroup
+// plan kernel writes the decode request lists, the workgroup start table and
+// the prefill items from the device copies of the same metadata, so no
+// host-to-device copy is needed.
 #pragma once
 
 #include <stddef.h>
@@ -23,27 +30,42 @@
 
 namespace ra {
 
+// Upper bound of decode workgroups per call (all head groups together); it
+// sizes the partial-result slots of the workspace independently of the GPU.
+constexpr int kMaxDecodeWorkgroups = 512;
+
 struct Plan {
     // classification
     int n_decode_reqs = 0, n_prefill_reqs = 0;
     // decode
-    int split_tokens = 0;       // keys per decode split (multiple of the page size)
-    int n_decode_items = 0;     // (request, split) pairs; each runs Hkv wavefronts
-    int n_merge = 0;            // decode requests with more than one split
-    int n_parts = 0;            // partial results written by split requests
+    int n_decode_pages = 0;     // NP: pages of all decode requests
+    int decode_hw = 0;          // kv heads per decode workgroup
+    int decode_hgroups = 0;     // Hkv / decode_hw
+    int decode_wg_cap = 0;      // workgroups per head group the workspace is sized for
     // prefill
     int q_tile = 0;             // query tokens per prefill work item
     int n_prefill_items = 0;    // (request, kv head, query tile) triples
     // which path runs
     bool specialised_ok = false;
     // workspace layout (byte offsets, 256-aligned)
-    size_t off_decode = 0, off_merge = 0, off_prefill = 0;
+    size_t off_dreq = 0, off_dpfx = 0, off_wstart = 0;
     size_t off_part_o = 0, off_part_ml = 0;
+    size_t off_ppfx = 0, off_prefill = 0;
     size_t workspace_bytes = 0;
 };
 
+// The decode work description the decode kernel reads (all in the workspace).
+struct DecodeWork {
+    const int32_t *dreq;    // [nd]      request id of the i-th decode request
+    const int32_t *dpfx;    // [nd + 1]  first flat page of decode request i
+    const int32_t *wstart;  // [nwg]     decode request holding workgroup b's first page
+    float *part_o;          // [nhg][nwg][2][HW*G][D] partial o (unnormalised)
+    float *part_ml;         // [nhg][nwg][2][HW*G][2] partial (m, l)
+    int nd, np, nwg;        // decode requests, flat pages, workgroups per head group
+};
+
 // Optional hipEvents recorded at the stage boundaries of one call.
-constexpr int kNumStageEvents = 5;
+constexpr int kNumStageEvents = 4;
 struct StageEvents {
     void *const *events;
     hipStream_t stream;
@@ -61,10 +83,9 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
 // Kernels of the specialised path.
 // kv heads per decode workgroup for this head_dim and kv-head count.
 int decode_heads_per_group(int D, int Hkv);
-hipError_t launch_decode(const Params &p, const Plan &plan, const int4 *items, float *part_o,
-                         float *part_ml, hipStream_t stream);
-hipError_t launch_merge(const Params &p, const Plan &plan, const int4 *items, const float *part_o,
-                        const float *part_ml, hipStream_t stream);
+// Decode workgroups per head group to launch on the current device.
+hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg);
+hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream);
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items,
                           hipStream_t stream);
 bool prefill_supports(int D, int G);

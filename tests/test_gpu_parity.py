@@ -117,6 +117,11 @@ EDGES = {
     "one_token_prefill_tail": ([129, 2, 1], [0, 1, 255], 8, 2, 128),
     "long_decode_many_splits": ([1, 1, 1], [9000, 2500, 17], 32, 8, 128),
     "d256_long": ([1, 70], [2100, 33], 16, 8, 256),
+    # many short decode requests per decode workgroup, next to long ones that
+    # several workgroups share
+    "many_short_decodes": ([1] * 40, [(7 * i) % 45 for i in range(39)] + [3000], 32, 8, 128),
+    "short_decodes_d256": ([1] * 24, [(5 * i) % 33 for i in range(23)] + [1500], 16, 8, 256),
+    "short_decodes_g1": ([1] * 30, [(3 * i) % 50 for i in range(30)], 4, 4, 64),
 }
 
 
@@ -127,6 +132,17 @@ def test_edge_cases(name, variant):
     b = build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, seed=sum(map(ord, name)),
                     num_pages=sum((x + y + 15) // 16 for x, y in zip(q, c)) + 2, name=name)
     check_small(b, variant)
+
+
+@pytest.mark.parametrize("wgs", [1, 3])
+def test_decode_with_few_workgroups(wgs, monkeypatch):
+    """Few decode workgroups (forced): each streams thousands of pages, so it
+    walks many requests and restages its page ids in LDS more than once."""
+    monkeypatch.setenv("RA_DECODE_WGS", str(wgs))
+    ctx = [5000, 3, 1700, 16, 31, 4096, 900, 0, 2500]
+    b = build_batch([1] * len(ctx), ctx, num_q_heads=16, num_kv_heads=8, head_dim=128, seed=77,
+                    name=f"few_wgs_{wgs}")
+    check_small(b, "specialised")
 
 
 def test_fresh_decode_returns_v_new():
@@ -209,9 +225,29 @@ def test_page_permutation_invariance():
 
 
 def test_request_order_invariance():
+    """Reordering the requests permutes the output rows.  The decode work is
+    split over workgroups along the flat page list, whose cut points move with
+    the order, so the rows agree to rounding (both stay within the oracle's
+    tolerance) rather than bit for bit."""
     from tests.test_oracle import reorder_requests
     b = _mixed_small(23)
     order = np.random.default_rng(6).permutation(b.num_reqs)
+    nb, tok = reorder_requests(b, order)
+    o1, _, _ = run_gpu(b)
+    o2, _, _ = run_gpu(nb)
+    a1 = o1[torch.from_numpy(tok)].float()
+    a2 = o2.float()
+    assert float((a1 - a2).abs().max()) <= 2 * TOL
+    ref, _, _ = oracle_full(nb)
+    assert_close(o2, ref, "reordered")
+
+
+def test_prefill_rows_are_order_invariant_bitwise():
+    """Prefill rows do not depend on where a request sits in the batch."""
+    from tests.test_oracle import reorder_requests
+    b = random_batch(31, num_reqs=5, max_q=60, max_ctx=200, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, decode_frac=0.0)
+    order = np.random.default_rng(7).permutation(b.num_reqs)
     nb, tok = reorder_requests(b, order)
     o1, _, _ = run_gpu(b)
     o2, _, _ = run_gpu(nb)
