@@ -135,12 +135,13 @@ ra_status ra_forward_variant(const ra_shape *shape,
 
 /*
  * ra_forward_variant that also records caller-created hipEvent_t handles on
- * `stream` at the stage boundaries of the call, so that the caller can time
- * each kernel: events[0] before the first launch, then events[1..3] after
- * the plan, prefill and decode stages, in that order (a stage that does not
- * run still records its event, so its duration reads as ~0; the generic
- * variant runs as the prefill stage).  n_events must be 4; events are not
- * created, synchronised or destroyed by the library.
+ * `stream` at the kernel boundaries of the call, so that the caller can time
+ * each kernel: events[0] before the first launch, then events[1..4] after
+ * the plan kernel, the prefill kernel, the decode kernel and the decode
+ * merge kernel, in that order (a kernel that does not run still has its
+ * event recorded, so its duration reads as ~0; the generic variant runs as
+ * the prefill kernel).  n_events must be 5; events are not created,
+ * synchronised or destroyed by the library.
  */
 ra_status ra_forward_profiled(const ra_shape *shape,
                               const void *q, const void *k_new, const void *v_new,

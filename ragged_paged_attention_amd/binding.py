@@ -161,11 +161,11 @@ def forward(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_le
 # --------------------------------------------------------------------------
 # Per-stage timing (plumbing for the bench: hipEvents through libamdhip64).
 # --------------------------------------------------------------------------
-STAGES = ("plan", "prefill", "decode")
+STAGES = ("plan", "prefill", "decode", "merge")
 
 
 class StageTimer:
-    """Four hipEvents recorded by ra_forward_profiled at the stage boundaries."""
+    """Five hipEvents recorded by ra_forward_profiled at the kernel boundaries."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
@@ -174,8 +174,8 @@ class StageTimer:
                                                  ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.events = (ctypes.c_void_p * 4)()
-        for k in range(4):
+        self.events = (ctypes.c_void_p * 5)()
+        for k in range(5):
             ev = ctypes.c_void_p()
             if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -183,7 +183,7 @@ class StageTimer:
 
     def stage_ms(self) -> dict:
         """Milliseconds of each stage of the last profiled call (waits for it)."""
-        if self.hip.hipEventSynchronize(self.events[3]) != 0:
+        if self.hip.hipEventSynchronize(self.events[4]) != 0:
             raise RuntimeError("hipEventSynchronize failed")
         out = {}
         for k, name in enumerate(STAGES):
@@ -194,7 +194,7 @@ class StageTimer:
         return out
 
     def close(self):
-        for k in range(4):
+        for k in range(5):
             if self.events[k]:
                 self.hip.hipEventDestroy(self.events[k])
                 self.events[k] = None
@@ -229,6 +229,6 @@ class Prepared:
             st = self.lib.ra_forward_variant(*self.args, ctypes.c_void_p(stream), self.variant)
         else:
             st = self.lib.ra_forward_profiled(*self.args, ctypes.c_void_p(stream), self.variant,
-                                              timer.events, 4)
+                                              timer.events, 5)
         _check(st)
         return self.out

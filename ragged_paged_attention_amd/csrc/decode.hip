@@ -452,21 +452,37 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
     const int hl = w * G + n16;  // q head inside the head group
     const int r = ld_meta(dw.dreq, i);
     const int t0 = ld_meta(p.cu_q_lens, r);
-    float M = -INFINITY;
-    for (int bb = b_first; bb <= b_last; ++bb)
-        M = fmaxf(M, dw.part_ml[((size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl) * 2]);
+    // One pass with a running max; the slots are read kU at a time so that
+    // their loads are in flight together (a request rarely spans more than
+    // two or three workgroups).
+    constexpr int kU = 4;
+    float M = -INFINITY, den = 0.f;
     float4_t acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int bb = b_first; bb <= b_last; ++bb) {
-        const size_t sidx = (size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl;
-        const float wgt = fast_exp2(dw.part_ml[sidx * 2] - M);
-        den += wgt * dw.part_ml[sidx * 2 + 1];
-        const float *prow = dw.part_o + sidx * D;
+    for (int b0 = b_first; b0 <= b_last; b0 += kU) {
+        float ms[kU], ls[kU];
+        float4_t os[kU][MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            acc[mb] += wgt * *reinterpret_cast<const float4_t *>(prow + 16 * mb + 4 * kg);
+        for (int u = 0; u < kU; ++u) {
+            const int bb = min(b0 + u, b_last);
+            const size_t sidx = (size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl;
+            ms[u] = dw.part_ml[sidx * 2];
+            ls[u] = dw.part_ml[sidx * 2 + 1];
+            const float *prow = dw.part_o + sidx * D;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) os[u][mb] = *reinterpret_cast<const float4_t *>(prow + 16 * mb + 4 * kg);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (b0 + u > b_last) break;
+            const float mn = fmaxf(M, ms[u]);
+            const float a = fast_exp2(M - mn), wgt = fast_exp2(ms[u] - mn);
+            den = den * a + wgt * ls[u];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = acc[mb] * a + wgt * os[u][mb];
+            M = mn;
+        }
     }
     const float inv = 1.f / den;
     bf16_t *orow = p.out + ((size_t)t0 * p.Hq + (hg * HW + w) * G + n16) * D;
@@ -509,13 +525,16 @@ hipError_t decode_capacity(int *cap) {
 }
 
 template <int D, int HW, int PF>
-hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t stream) {
+hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t stream,
+                             const StageEvents &ev) {
     hipError_t e = configure_decode<D, HW, PF>();
     if (e != hipSuccess) return e;
     const dim3 grid(p.Hkv / HW, dw.nwg);
     const size_t lds = DecodeCfg<D, HW>::LDS_BYTES;
     hipLaunchKernelGGL((decode_kernel<D, HW, PF>), grid, dim3(64 * HW), lds, stream, p, dw);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = ev.record(3);
     if (e != hipSuccess) return e;
     const dim3 mgrid(p.Hkv / HW, dw.nd);
     hipLaunchKernelGGL((decode_merge_kernel<D, HW>), mgrid, dim3(64 * HW), 0, stream, p, dw);
@@ -536,9 +555,10 @@ hipError_t with_hw(int Hkv, F &&f) {
 }
 
 template <int D, int PF>
-hipError_t launch_decode_d(const Params &p, const DecodeWork &dw, hipStream_t stream) {
+hipError_t launch_decode_d(const Params &p, const DecodeWork &dw, hipStream_t stream,
+                           const StageEvents &ev) {
     return with_hw<D, PF>(p.Hkv, [&](auto hw) {
-        return launch_decode_cfg<D, decltype(hw)::value, PF>(p, dw, stream);
+        return launch_decode_cfg<D, decltype(hw)::value, PF>(p, dw, stream, ev);
     });
 }
 
@@ -581,11 +601,12 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg) {
     return hipSuccess;
 }
 
-hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream) {
+hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream,
+                         const StageEvents &ev) {
     switch (p.D) {
-        case 64: return launch_decode_d<64, RA_DECODE_PF64>(p, dw, stream);
-        case 128: return launch_decode_d<128, RA_DECODE_PF128>(p, dw, stream);
-        case 256: return launch_decode_d<256, RA_DECODE_PF256>(p, dw, stream);
+        case 64: return launch_decode_d<64, RA_DECODE_PF64>(p, dw, stream, ev);
+        case 128: return launch_decode_d<128, RA_DECODE_PF128>(p, dw, stream, ev);
+        case 256: return launch_decode_d<256, RA_DECODE_PF256>(p, dw, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

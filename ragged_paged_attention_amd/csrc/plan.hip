@@ -87,8 +87,13 @@ __device__ void scan3(int (*buf)[kPlanThreads], int v[3], int tot[3]) {
     __syncthreads();
 }
 
-// Index of the last entry <= x of the non-decreasing array a[0..n).
-__device__ int last_le(const int32_t *a, int n, int x) {
+// Prefix arrays up to this many entries are searched in LDS.
+constexpr int kPlanLds = 4096;
+
+// Index of the last entry <= x of the non-decreasing array a[0..n) (global
+// memory or LDS).
+template <typename P>
+__device__ int last_le(P a, int n, int x) {
     int lo = 0, hi = n;  // answer in [lo, hi)
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -105,6 +110,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t *cu, const int32_t *ctx, int R, int S, int q_tile, int Hkv, int nwg,
     int32_t *dreq, int32_t *dpfx, int32_t *wstart, int32_t *ppfx, int4 *pre) {
     __shared__ int buf[3][kPlanThreads];
+    __shared__ int dpfx_l[kPlanLds + 1], ppfx_l[kPlanLds + 1];  // LDS copies for the searches
     const int tid = threadIdx.x;
     int base[3] = {0, 0, 0};  // decode requests, decode pages, prefill items
     for (int r0 = 0; r0 < R; r0 += kPlanThreads) {
@@ -122,26 +128,35 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         int ex[3] = {n[0], n[1], n[2]}, tot[3];
         scan3(buf, ex, tot);
         if (n[0]) {
-            dreq[base[0] + ex[0]] = r;
-            dpfx[base[0] + ex[0]] = base[1] + ex[1];
+            const int i = base[0] + ex[0];
+            dreq[i] = r;
+            dpfx[i] = base[1] + ex[1];
+            if (i <= kPlanLds) dpfx_l[i] = base[1] + ex[1];
         }
-        if (r < R) ppfx[r] = base[2] + ex[2];
+        if (r < R) {
+            ppfx[r] = base[2] + ex[2];
+            if (r <= kPlanLds) ppfx_l[r] = base[2] + ex[2];
+        }
         for (int k = 0; k < 3; ++k) base[k] += tot[k];
     }
     const int nd = base[0], np = base[1], npre = base[2];
     if (tid == 0) {
         dpfx[nd] = np;
         ppfx[R] = npre;
+        if (nd <= kPlanLds) dpfx_l[nd] = np;
+        if (R <= kPlanLds) ppfx_l[R] = npre;
     }
     __syncthreads();  // the arrays above are read back below
     for (int b = tid; b < nwg && nd > 0; b += kPlanThreads) {
         const int g0 = (int)(((long long)b * np) / nwg);
-        wstart[b] = last_le(dpfx, nd + 1, g0);
+        wstart[b] = nd <= kPlanLds ? last_le(dpfx_l, nd + 1, g0) : last_le(dpfx, nd + 1, g0);
     }
     for (int k = tid; k < npre; k += kPlanThreads) {
-        const int r = last_le(ppfx, R + 1, k);
-        const int local = k - ppfx[r];
-        const int ntiles = (ppfx[r + 1] - ppfx[r]) / Hkv;
+        const int r = R <= kPlanLds ? last_le(ppfx_l, R + 1, k) : last_le(ppfx, R + 1, k);
+        const int p0 = R <= kPlanLds ? ppfx_l[r] : ppfx[r];
+        const int p1 = R <= kPlanLds ? ppfx_l[r + 1] : ppfx[r + 1];
+        const int local = k - p0;
+        const int ntiles = (p1 - p0) / Hkv;
         const int rank = local / Hkv, hk = local - rank * Hkv;
         const int qt = ntiles - 1 - rank;  // longest key ranges first
         pre[k] = make_int4(r, hk, qt * q_tile, 0);
@@ -178,8 +193,14 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     if (err == hipSuccess) err = ev.record(1);
     if (err == hipSuccess && plan.n_prefill_items > 0) err = launch_prefill(p, plan, pre, stream);
     if (err == hipSuccess) err = ev.record(2);
-    if (err == hipSuccess && dw.nd > 0) err = launch_decode(p, dw, stream);
-    if (err == hipSuccess) err = ev.record(3);
+    if (err == hipSuccess) {
+        if (dw.nd > 0) {
+            err = launch_decode(p, dw, stream, ev);  // records event 3 between its kernels
+        } else {
+            err = ev.record(3);
+        }
+    }
+    if (err == hipSuccess) err = ev.record(4);
     return err;
 }
 

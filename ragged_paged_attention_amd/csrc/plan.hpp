@@ -65,7 +65,7 @@ struct DecodeWork {
 };
 
 // Optional hipEvents recorded at the stage boundaries of one call.
-constexpr int kNumStageEvents = 4;
+constexpr int kNumStageEvents = 5;
 struct StageEvents {
     void *const *events;
     hipStream_t stream;
@@ -85,7 +85,9 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
 int decode_heads_per_group(int D, int Hkv);
 // Decode workgroups per head group to launch on the current device.
 hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg);
-hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream);
+// Launches the decode kernel, records event 3, launches the merge kernel.
+hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream,
+                         const StageEvents &ev);
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items,
                           hipStream_t stream);
 bool prefill_supports(int D, int G);

@@ -122,6 +122,10 @@ EDGES = {
     "many_short_decodes": ([1] * 40, [(7 * i) % 45 for i in range(39)] + [3000], 32, 8, 128),
     "short_decodes_d256": ([1] * 24, [(5 * i) % 33 for i in range(23)] + [1500], 16, 8, 256),
     "short_decodes_g1": ([1] * 30, [(3 * i) % 50 for i in range(30)], 4, 4, 64),
+    # more requests than the plan kernel keeps in LDS (its searches then run
+    # over global memory), decode and prefill mixed
+    "many_requests": ([1 if i % 7 else 3 for i in range(4500)], [(11 * i) % 37 for i in range(4500)],
+                      8, 2, 64),
 }
 
 
