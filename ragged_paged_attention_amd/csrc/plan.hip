@@ -33,7 +33,7 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     pl.decode_hw = decode_heads_per_group(D, Hkv);
     pl.decode_hgroups = Hkv / pl.decode_hw;
     pl.decode_wg_cap = pl.n_decode_reqs ? std::max(1, kMaxDecodeWorkgroups / pl.decode_hgroups) : 0;
-    pl.q_tile = prefill_supports(D, G) ? 128 / G : 0;
+    pl.q_tile = prefill_supports(D, G) ? prefill_rows(D) / G : 0;
     pl.specialised_ok = (s.page_size == 16) && (D == 64 || D == 128 || D == 256) && G <= 16 &&
                         (pl.n_prefill_reqs == 0 || pl.q_tile > 0);
     for (int r = 0; r < R; ++r) {

@@ -91,5 +91,7 @@ hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stre
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items,
                           hipStream_t stream);
 bool prefill_supports(int D, int G);
+// Query rows (heads x tokens) of one prefill workgroup for this head_dim.
+int prefill_rows(int D);
 
 }  // namespace ra

@@ -1,23 +1,33 @@
 // prefill.hip -- the MFMA-bound kernel for prefill chunks (requests with more
 // than one new token), with the KV-cache update fused in.
 //
-// Work unit: one workgroup of 4 wavefronts per (request r, kv head hk, query
-// tile of Mq = 128/G tokens).  Its 128 query rows are the G query heads of
-// the group times the Mq tokens, so one K/V tile in LDS serves every head
-// that reads it (grouped-query attention).  Wave w owns rows 32w..32w+31.
+// Work unit: one workgroup of NW wavefronts per (request r, kv head hk, query
+// tile of ROWS/G tokens).  Its ROWS query rows are the G query heads of the
+// group times the tile's tokens, so one K/V tile in LDS serves every head
+// that reads it (grouped-query attention).  Wavefront w owns MW consecutive
+// rows (two 32-row halves when MW = 64): each K or V element it reads from
+// LDS feeds two MFMAs, which halves the LDS traffic per FLOP.
 //
-// Key tiles of N keys (64 for head_dim <= 128, 32 for 256) stream through
-// two LDS stages: while the MFMA units work on stage t, the next tile's
-// 16-byte global loads are in flight in registers, and land in the other
-// stage before the one barrier per tile.  Keys at positions < c_r come from
-// the cache through the page table, positions >= c_r from k_new/v_new.
+// Key tiles of N keys (32 or 64) stream through a ring of NSTAGE LDS stages with
+// direct-to-LDS 16-byte loads (global_load_lds_dwordx4): no registers hold
+// data in flight, and NSTAGE - 1 tiles are in flight while one is used.  In
+// one tile every wavefront loads N/4 key rows (inside one page of the paged
+// cache, so their page id is one scalar load); lane l of a 1 KiB load lands at byte
+// 16 l, and each lane fetches the chunk that makes the LDS layout XOR
+// swizzled (chunk c of row j at position c ^ (j & SWM)), so the MFMA-layout
+// reads below are free of bank conflicts.  Keys at positions < c_r come from
+// the cache through the page table, positions >= c_r from k_new/v_new;
+// positions past the tile's last visible key read that key again (finite,
+// and masked).
 //
-// Per tile and wave (v_mfma_f32_32x32x16_bf16 throughout):
+// Per tile and wavefront (v_mfma_f32_32x32x16_bf16 throughout):
 //   S^T[key][row] = K . Q^T     A = K rows from LDS (16 B per lane),
 //                               B = Q^T held in registers for the whole loop;
 //   online softmax on S^T       each lane owns one query row: the row max is
-//                               an in-lane max plus one cross-half step, and
-//                               the rescale of O^T is lane-local;
+//                               an in-lane max plus one cross-half step; the
+//                               scale is folded into one FMA before exp2; the
+//                               accumulator is rescaled only when a row max
+//                               grows past a headroom (lazy rescale);
 //   O^T[d][row] += V^T . P^T    B = P^T straight from the S^T accumulators
 //                               (converted to bf16 with v_cvt_pk_bf16_f32),
 //                               A = V^T by ds_read_b64_tr_b16 from the
@@ -25,8 +35,8 @@
 //                               at 4 key rows x 4 column quads and lane j
 //                               receives column j of those 4 keys.
 // Causal masking: tiles beyond the last row's position are never loaded;
-// tiles beyond a wave's last position are skipped by that wave; the mask
-// is applied only on tiles that cross a row's limit.
+// tiles beyond a wavefront's last position are skipped by that wavefront; the
+// mask is applied only on tiles that cross a row's limit.
 // The workgroup copies the new K/V rows of its own query tokens into the
 // cache (each (token, kv head) row is written exactly once).
 #include "launch.hpp"
@@ -46,6 +56,19 @@ __device__ __forceinline__ short4_t lds_read_tr16(const bf16_t *p) {
         (__attribute__((address_space(3))) v4i16 *)(const_cast<bf16_t *>(p)));
 }
 
+// 16 bytes from global memory straight into LDS: lane l's chunk lands at
+// lds_base + 16 l (lds_base is the same for the whole wavefront).
+__device__ __forceinline__ void load_lds16(const bf16_t *g, bf16_t *lds_base) {
+    __builtin_amdgcn_global_load_lds((const void *)g, (__attribute__((address_space(3))) void *)lds_base,
+                                     16, 0, 0);
+}
+
+// Metadata the kernel never writes, read through the constant address space
+// (a scalar load when the address is uniform).
+__device__ __forceinline__ int ld_meta(const int32_t *a, size_t i) {
+    return ((const __attribute__((address_space(4))) int32_t *)a)[i];
+}
+
 __device__ __forceinline__ int wave_max_i(int x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
@@ -58,240 +81,332 @@ __device__ __forceinline__ int wave_min_i(int x) {
     return x;
 }
 
+// Headroom of the lazy softmax rescale, in log2 units.
+constexpr float kLazyLog2 = 8.f;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wavefront are outstanding (expcnt and lgkmcnt left at their maximum).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Tile shape per head_dim: query rows per wavefront (MW), wavefronts per
+// workgroup (NW), keys per tile (N) and workgroups resident per CU (OCC).
+#ifndef RA_PREFILL_MW128
+#define RA_PREFILL_MW128 32
+#endif
+#ifndef RA_PREFILL_NW128
+#define RA_PREFILL_NW128 8
+#endif
+#ifndef RA_PREFILL_N128
+#define RA_PREFILL_N128 64
+#endif
+#ifndef RA_PREFILL_OCC128
+#define RA_PREFILL_OCC128 1
+#endif
+
 template <int D>
-struct PrefillCfg {
-    static constexpr int N = D <= 128 ? 64 : 32;  // keys per tile
-    static constexpr int KS = D / 16;              // QK k-steps
-    static constexpr int MBK = N / 32;             // 32-key blocks of S^T per tile
-    static constexpr int MD = D / 32;              // 32-wide head_dim blocks of O^T
-    static constexpr int RS = D + 16;              // LDS row stride (elements)
-    static constexpr int CH = D / 8;               // 16-byte chunks per row
-    static constexpr int LD = N * CH / 256;        // chunks per thread per tensor per tile
-    static constexpr int MIN_WAVES = D <= 128 ? 2 : 1;
+struct PrefillShape;
+template <>
+struct PrefillShape<64> {
+    static constexpr int MW = 64, NW = 4, N = 64, OCC = 1;
+};
+template <>
+struct PrefillShape<128> {
+    static constexpr int MW = RA_PREFILL_MW128, NW = RA_PREFILL_NW128, N = RA_PREFILL_N128,
+                         OCC = RA_PREFILL_OCC128;
+};
+template <>
+struct PrefillShape<256> {
+    static constexpr int MW = 32, NW = 4, N = 64, OCC = 1;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, PrefillCfg<D>::MIN_WAVES) void prefill_kernel(
+struct PrefillCfg {
+    using S = PrefillShape<D>;
+    static constexpr int MW = S::MW;                // query rows per wavefront
+    static constexpr int NW = S::NW;                // wavefronts per workgroup
+    static constexpr int N = S::N;                  // keys per tile
+    static constexpr int OCC = S::OCC;              // workgroups per CU (launch bound)
+    static constexpr int NTHR = 64 * NW;
+    static constexpr int NH = MW / 32;              // 32-row halves per wavefront
+    static constexpr int ROWS = NW * MW;            // query rows per workgroup
+    static constexpr int KB = N / 32;               // 32-key blocks of S^T
+    static constexpr int KS = D / 16;               // 16-dim k-steps of QK^T
+    static constexpr int MD = D / 32;               // 32-dim blocks of O^T
+    static constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
+    static constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // K chunk swizzle mask
+    static constexpr int VSS = CPR >= 16 ? 4 : 2;   // V chunk swizzle step
+    static constexpr int TILE = N * D;              // elements of one K (or V) tile
+    static constexpr int NSTAGE = D <= 128 ? 3 : 2; // LDS ring depth
+    static constexpr int RW = N / NW;               // key rows each wavefront loads per tile
+    static constexpr int RPI = 64 / CPR;            // rows per 1 KiB wavefront load
+    static constexpr int IPW = RW / RPI;            // loads per wavefront per tensor and tile
+    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * 2 * TILE * sizeof(bf16_t);
+    static_assert(16 % RW == 0 && RW % RPI == 0 && IPW >= 1, "a wavefront's rows of a tile lie in one page");
+};
+
+template <int D>
+__global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefill_kernel(
     Params p, const int4 *__restrict__ items) {
     using C = PrefillCfg<D>;
-    constexpr int N = C::N, KS = C::KS, MBK = C::MBK, MD = C::MD, RS = C::RS, CH = C::CH,
-                  LD = C::LD;
+    constexpr int MW = C::MW, NH = C::NH, ROWS = C::ROWS, N = C::N, KB = C::KB, KS = C::KS,
+                  MD = C::MD, CPR = C::CPR, SWM = C::SWM, TILE = C::TILE, NSTAGE = C::NSTAGE,
+                  RW = C::RW, RPI = C::RPI, IPW = C::IPW, NTHR = C::NTHR, VSS = C::VSS;
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-    // smem: [stage 0: K | V][stage 1: K | V], each N x RS elements
+    // smem: NSTAGE stages of [K tile | V tile], each tile N rows x D, swizzled
 
     const int4 it = items[blockIdx.x];
     const int r = it.x;
     if (r < 0) return;
     const int hk = it.y, q0 = it.z;
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, n32 = l & 31, h2 = l >> 5;
-    const int Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv, Mq = 128 / G;
-    const int t0 = p.cu_q_lens[r];
-    const int qlen = p.cu_q_lens[r + 1] - t0;
-    const int c = p.context_lens[r];
+    // The wavefront index as a scalar (the compiler cannot see that tid >> 6
+    // is uniform), so that per-wavefront metadata loads are scalar loads.
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, n32 = l & 31, h2 = l >> 5;
+    const int Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv, QT = ROWS / G;
+    const int t0 = ld_meta(p.cu_q_lens, r);
+    const int qlen = ld_meta(p.cu_q_lens, r + 1) - t0;
+    const int c = ld_meta(p.context_lens, r);
     const int L = c + qlen;
-    const int tile_q = min(Mq, qlen - q0);
-    const int kv_end = p.causal ? c + q0 + tile_q : L;
+    const int tile_q = min(QT, qlen - q0);
+    const int kv_end = p.causal ? c + q0 + tile_q : L;  // keys 0 .. kv_end-1 are visible to someone
     const int ntiles = (kv_end + N - 1) / N;
-    const int32_t *ptab = p.page_table + (size_t)r * p.max_pages;
+    const size_t prow = (size_t)r * p.max_pages;
 
     // Fused KV-cache update: the new rows of this tile's tokens, kv head hk.
-    for (int idx = tid; idx < tile_q * CH; idx += 256) {
-        const int row = idx / CH, col = idx - row * CH;
+    for (int idx = tid; idx < tile_q * CPR; idx += NTHR) {
+        const int row = idx / CPR, col = idx - row * CPR;
         const int t = t0 + q0 + row;
-        const size_t dst = ((size_t)p.slot_mapping[t] * Hkv + hk) * D + 8 * col;
+        const size_t dst = ((size_t)ld_meta(p.slot_mapping, t) * Hkv + hk) * D + 8 * col;
         const size_t src = ((size_t)t * Hkv + hk) * D + 8 * col;
         *reinterpret_cast<uint4 *>(p.k_cache + dst) = *reinterpret_cast<const uint4 *>(p.k_new + src);
         *reinterpret_cast<uint4 *>(p.v_cache + dst) = *reinterpret_cast<const uint4 *>(p.v_new + src);
     }
 
-    // This lane's query row.
-    const int R = 32 * w + n32;
-    const int g = R / Mq, iq = R - g * Mq;
-    const bool row_valid = iq < tile_q;
-    const int i = q0 + (row_valid ? iq : 0);
-    const int head = hk * G + g;
-    const int lim = row_valid ? (p.causal ? c + i : L - 1) : kv_end - 1;  // last visible key
-    const int wave_end = wave_max_i(row_valid ? lim : -1) + 1;
-    const int wave_lim_min = wave_min_i(row_valid ? lim : 0x7fffffff);
-
-    // Q^T as the B operand: lane holds q[t0 + i][head][16ks + 8h2 .. +8].
-    short8_t qb[KS];
-    {
-        const bf16_t *qrow = p.q + ((size_t)(t0 + i) * Hq + head) * D + 8 * h2;
+    // This lane's query rows (one per half): row R = MW w + 32 h + n32 is head
+    // g = R / QT, token i = R % QT of the tile.
+    int lim[NH];      // last visible key of the row
+    bool rvalid[NH];
+    short8_t qb[NH][KS];
+    int wave_end = 0, wave_lim_min = 0x7fffffff;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const int R = MW * w + 32 * h + n32;
+        const int g = R / QT, iq = R - g * QT;
+        rvalid[h] = iq < tile_q;
+        const int i = q0 + (rvalid[h] ? iq : 0);
+        lim[h] = rvalid[h] ? (p.causal ? c + i : L - 1) : -1;
+        wave_end = max(wave_end, lim[h] + 1);
+        if (rvalid[h]) wave_lim_min = min(wave_lim_min, lim[h]);
+        // Q^T as the B operand: lane holds q[t0 + i][hk*G + g][16ks + 8h2 .. +8].
+        const bf16_t *qrow = p.q + ((size_t)(t0 + i) * Hq + hk * G + g) * D + 8 * h2;
         const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const short8_t x = *reinterpret_cast<const short8_t *>(qrow + 16 * ks);
-            qb[ks] = row_valid ? x : z;
+            qb[h][ks] = rvalid[h] ? x : z;
         }
     }
+    wave_end = wave_max_i(wave_end);
+    wave_lim_min = wave_min_i(wave_lim_min);
 
-    // Register-staged tile loads (16 B chunks, consecutive threads along a row).
-    short8_t kreg[LD], vreg[LD];
-    auto load_tile = [&](int tile) {
-        const int j0 = tile * N;
-        const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+    // Direct-to-LDS loads of tile `tile` into stage `stage`: wavefront w loads
+    // key rows RW w .. RW w + RW - 1 (inside one page) of the K and V tiles.
+    const int lrow = l / CPR, lpc = l - lrow * CPR;  // row inside a 1 KiB load, physical chunk
+    // K tiles: chunk c of row j sits at c ^ (j & SWM), so that the 16 rows a
+    // 16-lane group reads with ds_read_b128 hit 16 different bank groups.  V
+    // tiles: chunk c of row j sits at c ^ VSS (j & 3), so that the 4 rows x
+    // 2 chunks a 16-lane group reads with ds_read_b64_tr_b16 (and the next
+    // group's 2 chunks) hit different banks; every read of a lane then sits
+    // at a fixed per-lane offset plus an immediate.
+    auto v_swizzle = [](int row) { return ((row & 3) * VSS) & SWM; };
+    // The four tensor bases as values (a select between struct fields could
+    // become a load of the field, which would wait for every load in flight).
+    const bf16_t *const kcache = p.k_cache, *const vcache = p.v_cache;
+    const bf16_t *const knew = p.k_new + (size_t)t0 * Hkv * D, *const vnew = p.v_new + (size_t)t0 * Hkv * D;
+    auto load_tile = [&](int tile, int stage) {
+        const int jw = tile * N + RW * w;                 // first key row of this wavefront
+        const int jp = min(jw, kv_end - 1);               // a visible position of the same page
+        const size_t page = (size_t)ld_meta(p.page_table, prow + jp / 16);
+        bf16_t *kst = smem + stage * 2 * TILE + RW * w * D;
 #pragma unroll
-        for (int k = 0; k < LD; ++k) {
-            const int q = tid + 256 * k;
-            const int row = q / CH, col = q - row * CH;
-            const int j = j0 + row;
-            const bool valid = j < kv_end;
-            const int je = valid ? j : kv_end - 1;
-            size_t rowaddr;
-            if (je < c) {
-                const size_t page = (size_t)ptab[je >> 4];
-                rowaddr = ((page * 16 + (je & 15)) * Hkv + hk) * D;
-            } else {
-                rowaddr = (((size_t)t0 + (je - c)) * Hkv + hk) * D;
-            }
-            const bool from_cache = je < c;
-            const bf16_t *kb = from_cache ? p.k_cache : p.k_new;
-            const bf16_t *vb = from_cache ? p.v_cache : p.v_new;
-            const short8_t xk = *reinterpret_cast<const short8_t *>(kb + rowaddr + 8 * col);
-            const short8_t xv = *reinterpret_cast<const short8_t *>(vb + rowaddr + 8 * col);
-            kreg[k] = valid ? xk : z;
-            vreg[k] = valid ? xv : z;
-        }
-    };
-    auto store_tile = [&](int stage) {
-        bf16_t *ks = smem + stage * 2 * N * RS;
-        bf16_t *vs = ks + N * RS;
-#pragma unroll
-        for (int k = 0; k < LD; ++k) {
-            const int q = tid + 256 * k;
-            const int row = q / CH, col = q - row * CH;
-            *reinterpret_cast<short8_t *>(ks + row * RS + 8 * col) = kreg[k];
-            *reinterpret_cast<short8_t *>(vs + row * RS + 8 * col) = vreg[k];
+        for (int u = 0; u < IPW; ++u) {
+            const int kr = RPI * u + lrow;                // row inside the wavefront's RW
+            const int j = min(jw + kr, kv_end - 1);       // rows past the end repeat the last key
+            const int row = RW * w + kr;                  // row inside the tile
+            const int lk = lpc ^ (row & SWM);             // logical K chunk landing at lpc
+            const int lv = lpc ^ v_swizzle(row);          // logical V chunk landing at lpc
+            const size_t crow = ((page * 16 + (j & 15)) * Hkv + hk) * D;
+            const size_t nrow = ((size_t)(j - c) * Hkv + hk) * D;
+            const bool cached = j < c;
+            load_lds16((cached ? kcache + crow : knew + nrow) + 8 * lk, kst + RPI * u * D);
+            load_lds16((cached ? vcache + crow : vnew + nrow) + 8 * lv, kst + TILE + RPI * u * D);
         }
     };
 
-    float16_t o[MD];
+    float16_t o[NH][MD];
 #pragma unroll
-    for (int md = 0; md < MD; ++md)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[md][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[h][md][e] = 0.f;
+    float m_run[NH], l_run[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+    }
     const float sl2 = p.scale_log2;
-    // Transposing-read lane address inside a V tile: row 4h2 + (j>>2), column
-    // 16*(n32>>4) + 4*(j&3) with j = l & 15.
-    const int vt_off = (4 * h2 + ((l & 15) >> 2)) * RS + 16 * (n32 >> 4) + 4 * (l & 3);
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // Per-lane LDS offsets (elements) of the MFMA-layout reads, fixed for the
+    // whole loop: K row n32 (+ 32 kb), dim chunk 2ks + h2; V^T rows
+    // 4h2 + (l & 15) / 4 (+ 16 s16, + 8 for the upper 4 keys), dims
+    // 32md + 16 (n32 / 16) + 4 (l & 3) .. +4.
+    int koff[KS], voff[MD];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = n32 * D + 8 * ((2 * ks + h2) ^ (n32 & SWM));
+    {
+        const int vr0 = 4 * h2 + ((l & 15) >> 2);
+        const int vc = 16 * (n32 >> 4) + 4 * (l & 3);
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+            const int col = 32 * md + vc;
+            voff[md] = vr0 * D + 8 * ((col >> 3) ^ v_swizzle(vr0)) + (col & 7);
+        }
+    }
+    const float16_t zero16 = {};
+
+    // Prologue: NSTAGE - 1 tiles in flight (tiles past the end reload the last
+    // one, so that every path issues the same loads and the wait counts below
+    // stay exact).
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s) load_tile(min(s, ntiles - 1), s);
 
     for (int tile = 0; tile < ntiles; ++tile) {
-        const int stage = tile & 1;
-        if (tile + 1 < ntiles) load_tile(tile + 1);
+        const int stage = tile % NSTAGE;
+        // Wait for this wavefront's loads of `tile` (the NSTAGE - 2 younger
+        // tiles may stay in flight), then for everyone's.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * IPW * (NSTAGE - 2)));
+        __syncthreads();
+        // The stage last used by tile - 1 is free now: refill it NSTAGE - 1 ahead.
+        load_tile(min(tile + NSTAGE - 1, ntiles - 1), (tile + NSTAGE - 1) % NSTAGE);
+
         const int j0 = tile * N;
         if (j0 < wave_end) {
-            const bf16_t *Ks = smem + stage * 2 * N * RS;
-            const bf16_t *Vs = Ks + N * RS;
-            float16_t s[MBK];
+            const bf16_t *Ks = smem + stage * 2 * TILE;
+            const bf16_t *Vs = Ks + TILE;
+            // S^T[key][row] = K . Q^T; each K read feeds every half.
+            float16_t s[NH][KB];
 #pragma unroll
-            for (int mb = 0; mb < MBK; ++mb) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) s[mb][e] = 0.f;
+            for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const short8_t a = *reinterpret_cast<const short8_t *>(
-                        Ks + (32 * mb + n32) * RS + 16 * ks + 8 * h2);
-                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], s[mb], 0, 0, 0);
+                    const short8_t a = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff[ks]);
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        s[h][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[h][ks], ks ? s[h][kb] : zero16, 0, 0, 0);
                 }
             }
-            // Scale into the exp2 domain; mask keys past this row's limit.
-            const bool need_mask = j0 + N - 1 > wave_lim_min;
-            float mx = -INFINITY;
+            // Online softmax per half; this lane holds keys
+            // j0 + 32kb + 8(e/4) + 4h2 + (e%4) of its row.
+            short8_t pb[NH][N / 16];
 #pragma unroll
-            for (int mb = 0; mb < MBK; ++mb) {
+            for (int h = 0; h < NH; ++h) {
+                if (j0 + N - 1 > wave_lim_min) {  // the tile crosses some row's last key
+                    const int thr = lim[h] - j0 - 4 * h2;  // key offset past which keys are masked
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float v = s[mb][e] * sl2;
-                    if (need_mask) {
-                        const int key = j0 + 32 * mb + 8 * (e >> 2) + 4 * h2 + (e & 3);
-                        v = key > lim ? -INFINITY : v;
-                    }
-                    s[mb][e] = v;
-                    mx = fmaxf(mx, v);
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            s[h][kb][e] = 32 * kb + 8 * (e >> 2) + (e & 3) > thr ? -INFINITY : s[h][kb][e];
                 }
-            }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - mn);
-            m_run = mn;
-            float lsum = 0.f;
-            short8_t pb[MBK][2];
+                float mx = -INFINITY;
 #pragma unroll
-            for (int mb = 0; mb < MBK; ++mb) {
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    uint32_t w4[4];
+                    for (int e = 0; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[h][kb][e]), s[h][kb][e + 1]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;  // raw max, then scaled (scale > 0)
+                if (__builtin_amdgcn_ballot_w64(mx > m_run[h] + kLazyLog2)) {
+                    const float mn = fmaxf(m_run[h], mx);
+                    const float alpha = fast_exp2(m_run[h] - mn);
+                    l_run[h] *= alpha;
 #pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        const float pa = fast_exp2(s[mb][8 * s2 + 2 * e2] - mn);
-                        const float pc = fast_exp2(s[mb][8 * s2 + 2 * e2 + 1] - mn);
-                        lsum += pa + pc;
-                        w4[e2] = cvt_pk_bf16(pa, pc);
-                    }
-                    pb[mb][s2] = __builtin_bit_cast(short8_t, w4);
+                    for (int md = 0; md < MD; ++md) o[h][md] *= alpha;
+                    m_run[h] = mn;
                 }
-            }
-            l_run = l_run * alpha + lsum;
+                const float nref = -m_run[h];
+                float lsum = 0.f;
 #pragma unroll
-            for (int md = 0; md < MD; ++md) o[md] *= alpha;
-            // O^T += V^T . P^T over the tile's keys, 16 per MFMA.
+                for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int mb = 0; mb < MBK; ++mb) {
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        uint32_t w4[4];
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const bf16_t *vb = Vs + (32 * mb + 16 * s2) * RS + vt_off;
-#pragma unroll
-                    for (int md = 0; md < MD; ++md) {
-                        const short4_t lo = lds_read_tr16(vb + 32 * md);
-                        const short4_t hi = lds_read_tr16(vb + 8 * RS + 32 * md);
-                        const short8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[mb][s2], o[md], 0, 0, 0);
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            const float pa = fast_exp2(fmaf(s[h][kb][8 * s2 + 2 * e2], sl2, nref));
+                            const float pc = fast_exp2(fmaf(s[h][kb][8 * s2 + 2 * e2 + 1], sl2, nref));
+                            lsum += pa + pc;
+                            w4[e2] = cvt_pk_bf16(pa, pc);
+                        }
+                        pb[h][2 * kb + s2] = __builtin_bit_cast(short8_t, w4);
                     }
+                }
+                l_run[h] += lsum;
+            }
+            // O^T += V^T . P^T over the tile's keys, 16 per MFMA; each V^T read
+            // feeds every half.
+#pragma unroll
+            for (int s16 = 0; s16 < N / 16; ++s16) {
+#pragma unroll
+                for (int md = 0; md < MD; ++md) {
+                    const bf16_t *va_lo = Vs + 16 * s16 * D + voff[md];
+                    const short4_t lo = lds_read_tr16(va_lo);
+                    const short4_t hi = lds_read_tr16(va_lo + 8 * D);
+                    const short8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        o[h][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h][s16], o[h][md], 0, 0, 0);
                 }
             }
         }
-        if (tile + 1 < ntiles) store_tile(stage ^ 1);
-        __syncthreads();
     }
+    // No direct-to-LDS load may still be writing when the workgroup retires.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-    if (row_valid) {
-        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32, 64);
+        if (!rvalid[h]) continue;
+        const int R = MW * w + 32 * h + n32;
+        const int g = R / QT, i = q0 + R - g * QT;
         const float inv = 1.f / l_tot;
-        bf16_t *orow = p.out + ((size_t)(t0 + i) * Hq + head) * D;
+        bf16_t *orow = p.out + ((size_t)(t0 + i) * Hq + hk * G + g) * D;
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 uint2 v;
-                v.x = cvt_pk_bf16(o[md][4 * q4] * inv, o[md][4 * q4 + 1] * inv);
-                v.y = cvt_pk_bf16(o[md][4 * q4 + 2] * inv, o[md][4 * q4 + 3] * inv);
+                v.x = cvt_pk_bf16(o[h][md][4 * q4] * inv, o[h][md][4 * q4 + 1] * inv);
+                v.y = cvt_pk_bf16(o[h][md][4 * q4 + 2] * inv, o[h][md][4 * q4 + 3] * inv);
                 *reinterpret_cast<uint2 *>(orow + 32 * md + 8 * q4 + 4 * h2) = v;
             }
         }
-    } else {
-        (void)__shfl_xor(l_run, 32, 64);
     }
 }
 
 template <int D>
 hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items, hipStream_t stream) {
     using C = PrefillCfg<D>;
-    const size_t lds = (size_t)2 * 2 * C::N * C::RS * sizeof(bf16_t);
     static bool configured = false;
     if (!configured) {
         hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    hipLaunchKernelGGL(prefill_kernel<D>, dim3(plan.n_prefill_items), dim3(256), lds, stream, p, items);
+    const size_t lds = C::LDS_BYTES;
+    hipLaunchKernelGGL(prefill_kernel<D>, dim3(plan.n_prefill_items), dim3(C::NTHR), lds, stream, p, items);
     return hipGetLastError();
 }
 
@@ -299,6 +414,15 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
 
 bool prefill_supports(int D, int G) {
     return (D == 64 || D == 128 || D == 256) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
+}
+
+int prefill_rows(int D) {
+    switch (D) {
+        case 64: return PrefillCfg<64>::ROWS;
+        case 128: return PrefillCfg<128>::ROWS;
+        case 256: return PrefillCfg<256>::ROWS;
+        default: return 0;
+    }
 }
 
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, hipStream_t stream) {
