@@ -91,27 +91,38 @@ constexpr float kLazyLog2 = 8.f;
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // Tile shape per head_dim: wavefronts per workgroup (NW), keys per tile (N),
-// LDS ring depth (NSTAGE) and workgroups resident per CU (OCC).  Every
-// wavefront owns 32 query rows.
+// LDS ring depth (NSTAGE), workgroups resident per CU (OCC) and query rows
+// per wavefront (MW: 32, or 64 as two halves that share every K/V read).
 template <int D>
 struct PrefillShape;
+#ifndef RA_PREFILL_MW128
+#define RA_PREFILL_MW128 32
+#endif
+#ifndef RA_PREFILL_NW128
+#define RA_PREFILL_NW128 8
+#endif
+#ifndef RA_PREFILL_N128
+#define RA_PREFILL_N128 64
+#endif
 template <>
 struct PrefillShape<64> {
-    static constexpr int NW = 8, N = 64, NSTAGE = 4, OCC = 1;
+    static constexpr int MW = 32, NW = 8, N = 64, NSTAGE = 4, OCC = 1;
 };
 template <>
 struct PrefillShape<128> {
-    static constexpr int NW = 8, N = 64, NSTAGE = 4, OCC = 1;
+    static constexpr int MW = RA_PREFILL_MW128, NW = RA_PREFILL_NW128, N = RA_PREFILL_N128,
+                         NSTAGE = 4, OCC = 1;
 };
 template <>
 struct PrefillShape<256> {
-    static constexpr int NW = 4, N = 32, NSTAGE = 4, OCC = 1;
+    static constexpr int MW = 32, NW = 4, N = 32, NSTAGE = 4, OCC = 1;
 };
 
 template <int D>
 struct PrefillCfg {
     using S = PrefillShape<D>;
-    static constexpr int MW = 32;                   // query rows per wavefront
+    static constexpr int MW = S::MW;                // query rows per wavefront
+    static constexpr int NH = MW / 32;              // 32-row halves per wavefront
     static constexpr int NW = S::NW;                // wavefronts per workgroup
     static constexpr int N = S::N;                  // keys per tile
     static constexpr int OCC = S::OCC;              // workgroups per CU (launch bound)
@@ -136,9 +147,9 @@ template <int D>
 __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefill_kernel(
     Params p, const int4 *__restrict__ items) {
     using C = PrefillCfg<D>;
-    constexpr int ROWS = C::ROWS, N = C::N, KB = C::KB, KS = C::KS, MD = C::MD, CPR = C::CPR,
-                  SWM = C::SWM, TILE = C::TILE, NSTAGE = C::NSTAGE, RW = C::RW, RPI = C::RPI,
-                  IPW = C::IPW, NTHR = C::NTHR, VSS = C::VSS;
+    constexpr int NH = C::NH, ROWS = C::ROWS, N = C::N, KB = C::KB, KS = C::KS, MD = C::MD,
+                  CPR = C::CPR, SWM = C::SWM, TILE = C::TILE, NSTAGE = C::NSTAGE, RW = C::RW,
+                  RPI = C::RPI, IPW = C::IPW, NTHR = C::NTHR, VSS = C::VSS, MW = C::MW;
     static_assert(NSTAGE >= 4, "tile t+1 is computed on while tile t+2 is in flight");
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     // smem: NSTAGE stages of [K tile | V tile], each tile N rows x D, swizzled
@@ -172,26 +183,33 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
         *reinterpret_cast<uint4 *>(p.v_cache + dst) = *reinterpret_cast<const uint4 *>(p.v_new + src);
     }
 
-    // This lane's query row R = 32 w + n32: head g = R / QT, token i = R % QT
-    // of the tile.
-    const int R = 32 * w + n32;
-    const int g = R / QT, iq = R - g * QT;
-    const bool rvalid = iq < tile_q;
-    const int qi = q0 + (rvalid ? iq : 0);
-    const int lim = rvalid ? (p.causal ? c + qi : L - 1) : -1;  // last visible key
-    short8_t qb[KS];
-    {
+    // This lane's query rows, one per half h: row R = MW w + 32 h + n32 is
+    // head g = R / QT, token i = R % QT of the tile.
+    int gh[NH], qi[NH], lim[NH];
+    bool rvalid[NH];
+    short8_t qb[NH][KS];
+    int lim_max = -1, lim_min = 0x7fffffff;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const int R = MW * w + 32 * h + n32;
+        gh[h] = R / QT;
+        const int iq = R - gh[h] * QT;
+        rvalid[h] = iq < tile_q;
+        qi[h] = q0 + (rvalid[h] ? iq : 0);
+        lim[h] = rvalid[h] ? (p.causal ? c + qi[h] : L - 1) : -1;  // last visible key
+        lim_max = max(lim_max, lim[h]);
+        if (rvalid[h]) lim_min = min(lim_min, lim[h]);
         // Q^T as the B operand: lane holds q[t0 + qi][hk*G + g][16ks + 8h2 .. +8].
-        const bf16_t *qrow = p.q + ((size_t)(t0 + qi) * Hq + hk * G + g) * D + 8 * h2;
+        const bf16_t *qrow = p.q + ((size_t)(t0 + qi[h]) * Hq + hk * G + gh[h]) * D + 8 * h2;
         const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const short8_t x = *reinterpret_cast<const short8_t *>(qrow + 16 * ks);
-            qb[ks] = rvalid ? x : z;
+            qb[h][ks] = rvalid[h] ? x : z;
         }
     }
-    const int wave_end = wave_max_i(lim + 1);  // keys this wavefront needs
-    const int wave_lim_min = wave_min_i(rvalid ? lim : 0x7fffffff);
+    const int wave_end = wave_max_i(lim_max + 1);  // keys this wavefront needs
+    const int wave_lim_min = wave_min_i(lim_min);
     const int ntw = min(ntiles, (wave_end + N - 1) / N);  // tiles this wavefront computes
 
     // Direct-to-LDS loads of tile `tile` into stage `stage`: wavefront w loads
@@ -247,89 +265,101 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
     const float16_t zero16 = {};
     const float sl2 = p.scale_log2;
 
-    float16_t o[MD];
+    float16_t o[NH][MD];
 #pragma unroll
-    for (int md = 0; md < MD; ++md) o[md] = zero16;
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[h][md] = zero16;
+    float m_run[NH], l_run[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+    }
 
-    // S^T[key][row] = K . Q^T for the tile in `stage`.
-    auto qk = [&](int stage, float16_t (&s)[KB]) {
+    constexpr int NE = KB * 16;            // scores per lane, half and tile
+    // Element e of a half's scores is s[e / 16][e % 16], key
+    // 32 (e / 16) + 8 ((e % 16) / 4) + 4 h2 + e % 4 of the tile.
+    auto key_of = [](int e) { return 32 * (e / 16) + 8 * ((e % 16) >> 2) + (e & 3); };
+
+    // S^T[key][row] = K . Q^T for the tile in `stage`; each K read feeds
+    // every half.
+    auto qk = [&](int stage, float16_t (&s)[NH][KB]) {
         const bf16_t *Ks = smem + stage * 2 * TILE;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const short8_t a = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff[ks]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], ks ? s[kb] : zero16, 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    s[h][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[h][ks], ks ? s[h][kb] : zero16, 0, 0, 0);
             }
-        }
     };
-    // Row max (scaled) of tile `tile`, masking keys past the row's last one
-    // when MASKED; this lane holds keys j0 + 32kb + 8(e/4) + 4h2 + (e%4).
-    auto rowmax = [&](auto masked, int tile, float16_t (&s)[KB]) {
+    // Row max (scaled) of tile `tile` for half h, masking keys past the row's
+    // last one when MASKED.
+    auto rowmax = [&](auto masked, int tile, int h, float16_t (&s)[KB]) {
         if constexpr (decltype(masked)::value) {
-            const int thr = lim - tile * N - 4 * h2;  // key offset past which keys are masked
+            const int thr = lim[h] - tile * N - 4 * h2;  // key offset past which keys are masked
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    s[kb][e] = 32 * kb + 8 * (e >> 2) + (e & 3) > thr ? -INFINITY : s[kb][e];
+            for (int e = 0; e < NE; ++e)
+                s[e / 16][e % 16] = key_of(e) > thr ? -INFINITY : s[e / 16][e % 16];
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[kb][e]), s[kb][e + 1]);
+        for (int e = 0; e < NE; e += 2) mx = fmaxf(fmaxf(mx, s[e / 16][e % 16]), s[e / 16][e % 16 + 1]);
         return fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;  // raw max, then scaled (scale > 0)
     };
     // Lazy rescale: the reference max moves only when a row max exceeds it by
     // more than kLazyLog2 (P <= 2^kLazyLog2 otherwise).
-    auto rescale = [&](float mx) {
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
-            const float mn = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - mn);
-            l_run *= alpha;
+    auto rescale = [&](int h, float mx) {
+        if (__builtin_amdgcn_ballot_w64(mx > m_run[h] + kLazyLog2)) {
+            const float mn = fmaxf(m_run[h], mx);
+            const float alpha = fast_exp2(m_run[h] - mn);
+            l_run[h] *= alpha;
 #pragma unroll
-            for (int md = 0; md < MD; ++md) o[md] *= alpha;
-            m_run = mn;
+            for (int md = 0; md < MD; ++md) o[h][md] *= alpha;
+            m_run[h] = mn;
         }
     };
     auto masked_tile = [&](int tile) { return tile * N + N - 1 > wave_lim_min; };
-    // P^T = exp2(S^T * scale - m) as bf16 B operands, and the row sums.
-    auto tail = [&](const float16_t (&s)[KB], short8_t (&pb)[N / 16]) {
-        const float nref = -m_run;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                uint32_t w4[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const float pa = fast_exp2(fmaf(s[kb][8 * s2 + 2 * e2], sl2, nref));
-                    const float pc = fast_exp2(fmaf(s[kb][8 * s2 + 2 * e2 + 1], sl2, nref));
-                    lsum += pa + pc;
-                    w4[e2] = cvt_pk_bf16(pa, pc);
-                }
-                pb[2 * kb + s2] = __builtin_bit_cast(short8_t, w4);
-            }
-        }
-        l_run += lsum;
-    };
-    // O^T += V^T . P^T over the tile in `stage`, 16 keys per MFMA.
-    auto pv = [&](int stage, const short8_t (&pb)[N / 16]) {
-        const bf16_t *Vs = smem + stage * 2 * TILE + TILE;
+    // P^T = exp2(S^T * scale - m) of half h as bf16 B operands, and row sums.
+    auto pack = [&](const float (&pe)[NE], short8_t (&pb)[N / 16]) {
 #pragma unroll
         for (int s16 = 0; s16 < N / 16; ++s16) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) w4[e2] = cvt_pk_bf16(pe[8 * s16 + 2 * e2], pe[8 * s16 + 2 * e2 + 1]);
+            pb[s16] = __builtin_bit_cast(short8_t, w4);
+        }
+    };
+    auto tail = [&](int h, const float16_t (&s)[KB], short8_t (&pb)[N / 16]) {
+        const float nref = -m_run[h];
+        float pe[NE], lsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            pe[e] = fast_exp2(fmaf(s[e / 16][e % 16], sl2, nref));
+            lsum += pe[e];
+        }
+        l_run[h] += lsum;
+        pack(pe, pb);
+    };
+    // O^T += V^T . P^T over the tile in `stage`, 16 keys per MFMA; each V^T
+    // read feeds every half.
+    auto pv = [&](int stage, const short8_t (&pb)[NH][N / 16]) {
+        const bf16_t *Vs = smem + stage * 2 * TILE + TILE;
+#pragma unroll
+        for (int s16 = 0; s16 < N / 16; ++s16)
 #pragma unroll
             for (int md = 0; md < MD; ++md) {
-                const bf16_t *va_lo = Vs + 16 * s16 * D + voff[md];
-                const short4_t lo = lds_read_tr16(va_lo);
-                const short4_t hi = lds_read_tr16(va_lo + 8 * D);
+                const bf16_t *v = Vs + 16 * s16 * D + voff[md];
+                const short4_t lo = lds_read_tr16(v);
+                const short4_t hi = lds_read_tr16(v + 8 * D);
                 const short8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s16], o[md], 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    o[h][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h][s16], o[h][md], 0, 0, 0);
             }
-        }
     };
 
     // One pipelined iteration, hand-interleaved in chunks that the compiler
@@ -338,23 +368,26 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
     //     MFMAs of tile t+1's scores for this k-step, and a share of tile t's
     //     exponentials (VALU);
     //   phase B, one chunk per (16-key step, 32-dim block): the V^T reads for
-    //     the next chunk, one MFMA of tile t's P.V, and a share of tile t+1's
+    //     the next chunk, the MFMAs of tile t's P.V, and a share of tile t+1's
     //     (masked) row max.
     // MFMAs are asynchronous, so the VALU work of each chunk runs while the
     // chunk's MFMAs occupy the matrix unit.
-    float16_t s_cur[KB];                   // scores of the tile being finished
-    constexpr int NE = KB * 16;            // scores per lane and tile
-    constexpr int EA = NE / KS;            // exponentials per phase-A chunk
-    constexpr int NB = (N / 16) * MD;      // phase-B chunks
-    constexpr int EB = NE / NB;            // row-max elements per phase-B chunk
-    static_assert(NE % KS == 0 && NE % NB == 0, "chunks must split the scores evenly");
-    auto step = [&](auto masked, int t, float16_t (&s_nxt)[KB], short8_t (&pb)[N / 16]) -> float {
+    float16_t s_cur[NH][KB];                // scores of the tile being finished
+    constexpr int EA = NH * NE / KS;        // exponentials per phase-A chunk
+    constexpr int NB = (N / 16) * MD;       // phase-B chunks
+    constexpr int EB = NH * NE / NB;        // row-max elements per phase-B chunk
+    static_assert((NH * NE) % KS == 0 && (NH * NE) % NB == 0, "chunks must split the scores evenly");
+    auto step = [&](auto masked, int t, float16_t (&s_nxt)[NH][KB], short8_t (&pb)[NH][N / 16],
+                    float (&mx)[NH]) {
         const bf16_t *Ks = smem + ((t + 1) % NSTAGE) * 2 * TILE;
         const bf16_t *Vs = smem + (t % NSTAGE) * 2 * TILE + TILE;
         // ---- phase A
-        const float nref = -m_run;
-        float lsum = 0.f;
-        float pe[NE];
+        float nref[NH], lsum[NH], pe[NH][NE];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            nref[h] = -m_run[h];
+            lsum[h] = 0.f;
+        }
         short8_t ka[2][KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) ka[0][kb] = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff[0]);
@@ -367,30 +400,30 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
             }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb], qb[ks], ks ? s_nxt[kb] : zero16, 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < NH; ++h)
+                    s_nxt[h][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb], qb[h][ks],
+                                                                           ks ? s_nxt[h][kb] : zero16, 0, 0, 0);
 #pragma unroll
             for (int x = 0; x < EA; ++x) {
-                const int e = ks * EA + x;
-                pe[e] = fast_exp2(fmaf(s_cur[e / 16][e % 16], sl2, nref));
-                lsum += pe[e];
+                const int f = ks * EA + x, h = f / NE, e = f % NE;
+                pe[h][e] = fast_exp2(fmaf(s_cur[h][e / 16][e % 16], sl2, nref[h]));
+                lsum[h] += pe[h][e];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        l_run += lsum;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                uint32_t w4[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2)
-                    w4[e2] = cvt_pk_bf16(pe[kb * 16 + 8 * s2 + 2 * e2], pe[kb * 16 + 8 * s2 + 2 * e2 + 1]);
-                pb[2 * kb + s2] = __builtin_bit_cast(short8_t, w4);
-            }
+        for (int h = 0; h < NH; ++h) {
+            l_run[h] += lsum[h];
+            pack(pe[h], pb[h]);
         }
         // ---- phase B
-        const int thr = lim - (t + 1) * N - 4 * h2;  // key offset past which tile t+1 is masked
-        float mx = -INFINITY;
+        int thr[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            thr[h] = lim[h] - (t + 1) * N - 4 * h2;  // key offset past which tile t+1 is masked
+            mx[h] = -INFINITY;
+        }
         short8_t va[2];
         {
             const short4_t lo = lds_read_tr16(Vs + voff[0]);
@@ -401,46 +434,48 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
         for (int j = 0; j < NB; ++j) {
             const int s16 = j / MD, md = j % MD;
             if (j + 1 < NB) {
-                const int s16n = (j + 1) / MD, mdn = (j + 1) % MD;
-                const bf16_t *v = Vs + 16 * s16n * D + voff[mdn];
+                const bf16_t *v = Vs + 16 * ((j + 1) / MD) * D + voff[(j + 1) % MD];
                 const short4_t lo = lds_read_tr16(v);
                 const short4_t hi = lds_read_tr16(v + 8 * D);
                 va[(j + 1) & 1] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1], pb[s16], o[md], 0, 0, 0);
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+                o[h][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1], pb[h][s16], o[h][md], 0, 0, 0);
 #pragma unroll
             for (int x = 0; x < EB; ++x) {
-                const int e = j * EB + x;
-                float v = s_nxt[e / 16][e % 16];
+                const int f = j * EB + x, h = f / NE, e = f % NE;
+                float v = s_nxt[h][e / 16][e % 16];
                 if constexpr (decltype(masked)::value) {
-                    const int kb = e / 16, ee = e % 16;
-                    v = 32 * kb + 8 * (ee >> 2) + (ee & 3) > thr ? -INFINITY : v;
-                    s_nxt[kb][ee] = v;
+                    v = key_of(e) > thr[h] ? -INFINITY : v;
+                    s_nxt[h][e / 16][e % 16] = v;
                 }
-                mx = fmaxf(mx, v);
+                mx[h] = fmaxf(mx[h], v);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        return fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) mx[h] = fmaxf(mx[h], __shfl_xor(mx[h], 32, 64)) * sl2;
     };
 
     // Prologue: NSTAGE - 1 tiles in flight (tiles past the end reload the last
     // one, so that every path issues the same loads and the wait counts below
     // stay exact); tile 0's scores and their row max.
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s) load_tile(min(s, ntiles - 1), s);
+    for (int st = 0; st < NSTAGE - 1; ++st) load_tile(min(st, ntiles - 1), st);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * IPW * (NSTAGE - 2)));
     __syncthreads();
     if (ntw > 0) {
         qk(0, s_cur);
-        const float mx = masked_tile(0) ? rowmax(std::true_type(), 0, s_cur)
-                                         : rowmax(std::false_type(), 0, s_cur);
-        rescale(mx);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const float mx = masked_tile(0) ? rowmax(std::true_type(), 0, h, s_cur[h])
+                                             : rowmax(std::false_type(), 0, h, s_cur[h]);
+            rescale(h, mx);
+        }
     }
 
-    // Software pipeline, one tile per iteration: the scores of tile t+1 are
-    // computed (MFMA) while the exponentials of tile t run (VALU), then tile
-    // t's P.V (MFMA) runs while the row maxima of tile t+1 are taken (VALU).
+    // Software pipeline, one tile per iteration (see step).
     for (int t = 0; t < ntiles; ++t) {
         // Tile t+1 must be in LDS; tiles t+2 .. t+NSTAGE-2 may stay in flight.
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * IPW * (NSTAGE - 3)));
@@ -448,16 +483,24 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
         // Tile t-1's stage is free now (everyone finished its P.V): refill it.
         load_tile(min(t + NSTAGE - 1, ntiles - 1), (t + NSTAGE - 1) % NSTAGE);
         if (t < ntw) {
-            short8_t pb[N / 16];
+            short8_t pb[NH][N / 16];
             if (t + 1 < ntw) {
-                float16_t s_nxt[KB];
-                const float mx = masked_tile(t + 1) ? step(std::true_type(), t, s_nxt, pb)
-                                                    : step(std::false_type(), t, s_nxt, pb);
-                rescale(mx);
+                float16_t s_nxt[NH][KB];
+                float mx[NH];
+                if (masked_tile(t + 1)) {
+                    step(std::true_type(), t, s_nxt, pb, mx);
+                } else {
+                    step(std::false_type(), t, s_nxt, pb, mx);
+                }
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
+                for (int h = 0; h < NH; ++h) {
+                    rescale(h, mx[h]);
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) s_cur[h][kb] = s_nxt[h][kb];
+                }
             } else {
-                tail(s_cur, pb);
+#pragma unroll
+                for (int h = 0; h < NH; ++h) tail(h, s_cur[h], pb[h]);
                 pv(t % NSTAGE, pb);
             }
         }
@@ -465,17 +508,19 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
     // No direct-to-LDS load may still be writing when the workgroup retires.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (rvalid) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32, 64);
+        if (!rvalid[h]) continue;
         const float inv = 1.f / l_tot;
-        bf16_t *orow = p.out + ((size_t)(t0 + qi) * Hq + hk * G + g) * D;
+        bf16_t *orow = p.out + ((size_t)(t0 + qi[h]) * Hq + hk * G + gh[h]) * D;
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 uint2 v;
-                v.x = cvt_pk_bf16(o[md][4 * q4] * inv, o[md][4 * q4 + 1] * inv);
-                v.y = cvt_pk_bf16(o[md][4 * q4 + 2] * inv, o[md][4 * q4 + 3] * inv);
+                v.x = cvt_pk_bf16(o[h][md][4 * q4] * inv, o[h][md][4 * q4 + 1] * inv);
+                v.y = cvt_pk_bf16(o[h][md][4 * q4 + 2] * inv, o[h][md][4 * q4 + 3] * inv);
                 *reinterpret_cast<uint2 *>(orow + 32 * md + 8 * q4 + 4 * h2) = v;
             }
         }
