@@ -125,6 +125,71 @@ def measured_traffic(stage: str, workload: str):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
+def counter_means(directory: str, counter: str):
+    """Mean value of `counter` per dispatch, per kernel name, from the
+    counter_collection.csv that `rocprofv3 --pmc` wrote under `directory`."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    acc = {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            tot, n = acc.get(row["Kernel_Name"], (0.0, 0))
+            acc[row["Kernel_Name"]] = (tot + float(row["Counter_Value"]), n + 1)
+    return {k: (tot / n, n) for k, (tot, n) in acc.items()}
+
+
+def ingest_counters(args):
+    """HBM bytes per launch of the decode and prefill kernels from two
+    FETCH_SIZE / WRITE_SIZE passes over a workload, each scaled by what the
+    same counter reads for a device-to-device copy of known size."""
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = args.ingest_counters
+    copy_kib = args.copy_calibration_mib * 1024.0
+    factors = {}
+    for ctr, d in (("FETCH_SIZE", cal_fetch_dir), ("WRITE_SIZE", cal_write_dir)):
+        means = counter_means(d, ctr)
+        name, (val, n) = max(means.items(), key=lambda kv: kv[1][1])  # the copy: most dispatches
+        factors[ctr] = copy_kib / val
+        print(f"calibration {ctr}: {name} x{n}, {val:.0f} KiB per dispatch for a "
+              f"{copy_kib:.0f} KiB copy -> factor {factors[ctr]:.4f}")
+    fetch, write = counter_means(fetch_dir, "FETCH_SIZE"), counter_means(write_dir, "WRITE_SIZE")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    for stage, kname in (("decode", "decode_kernel"), ("prefill", "prefill_kernel")):
+        keys = [k for k in fetch if k.split("<")[0].split("(")[0].strip() == kname]
+        if not keys:
+            continue
+        k = keys[0]
+        f_kib, n = fetch[k]
+        w_kib = write.get(k, (0.0, 0))[0]
+        total = (f_kib * factors["FETCH_SIZE"] + w_kib * factors["WRITE_SIZE"]) * 1024.0
+        db[f"{args.config}/{stage}"] = {
+            "kernel": k, "dispatches": n, "fetch_kib_raw": f_kib, "write_kib_raw": w_kib,
+            "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"],
+            "bytes_per_launch": total, "source_sha256_16": kernel_source_hash(stage)}
+        print(f"{args.config}/{stage}: {k} x{n}: FETCH {f_kib:.0f} KiB, WRITE {w_kib:.0f} KiB raw "
+              f"-> {total / 1e9:.4f} GB per launch")
+    with open(path, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+
+def copy_calibration(mib: int):
+    """Device-to-device copies of `mib` MiB: the known-size kernel that the
+    HBM counters are scaled by."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+
+
 def sub_batch(b: Batch, reqs) -> Batch:
     cu = b.cu_q_lens.tolist()
     toks = [t for r in reqs for t in range(cu[r], cu[r + 1])]
@@ -188,7 +253,15 @@ def main():
     ap.add_argument("--variant", default="auto", choices=list(binding.VARIANTS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-baseline budget (0 disables the oracle leg)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run 5 device-to-device copies of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="CPU only: turn rocprofv3 FETCH_SIZE / WRITE_SIZE passes over --config (and over "
+                         "--copy-calibration-mib) into profiles/traffic.json")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
@@ -196,6 +269,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
 
     log(f"[bench] building inputs for {args.config}")
     b = config(args.config)
