@@ -56,7 +56,7 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     pl.off_ppfx = off;
     off = align256(off + sizeof(int32_t) * ((size_t)R + 1));
     pl.off_prefill = off;
-    off = align256(off + sizeof(int4) * (size_t)pl.n_prefill_items);
+    off = align256(off + 2 * sizeof(int4) * (size_t)pl.n_prefill_items);
     // A batch without new tokens launches nothing and needs no workspace.
     pl.workspace_bytes = (nd == 0 && pl.n_prefill_reqs == 0) ? 0 : off;
     *plan = pl;
@@ -105,7 +105,9 @@ __device__ int last_le(P a, int n, int x) {
 // Writes, from the device metadata: the decode request list and its flat page
 // prefix, the first decode request of every decode workgroup, the
 // per-request prefix of prefill items and the prefill items themselves
-// (longest query tiles of a request first).  Mirrors make_plan.
+// (longest query tiles of a request first; two int4 per item:
+// {r, kv head, first query, first token}, {context, new tokens, 0, 0}).
+// Mirrors make_plan.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t *cu, const int32_t *ctx, int R, int S, int q_tile, int Hkv, int nwg,
     int32_t *dreq, int32_t *dpfx, int32_t *wstart, int32_t *ppfx, int4 *pre) {
@@ -159,7 +161,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         const int ntiles = (p1 - p0) / Hkv;
         const int rank = local / Hkv, hk = local - rank * Hkv;
         const int qt = ntiles - 1 - rank;  // longest key ranges first
-        pre[k] = make_int4(r, hk, qt * q_tile, 0);
+        const int t0 = cu[r], q = cu[r + 1] - t0;
+        pre[2 * k] = make_int4(r, hk, qt * q_tile, t0);
+        pre[2 * k + 1] = make_int4(ctx[r], q, 0, 0);
     }
 }
 
