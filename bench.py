@@ -236,11 +236,52 @@ def cpu_baseline(b: Batch, kind: str, budget_s: float):
         value, unit = algorithmic_bytes(b, reqs) / secs / 1e9, "GB/s"
     else:
         value, unit = algorithmic_flops(b, reqs) / secs / 1e12, "TFLOP/s"
+    cpu_model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                      if ln.startswith("model name")), "unknown")
     return {"value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model, "nproc": os.cpu_count(),
             "sample": (f"{'all' if n == b.num_reqs else f'first {n} of'} {b.num_reqs} requests "
                        f"({toks} new tokens) x {reps} pass(es), {secs:.2f} s per pass, fp64, "
                        f"OpenMP over (token, q head), cache copy + scatter included"),
             "tokens_per_s": toks / secs, "seconds": secs}
+
+
+def sweep_decode(args):
+    """Decode bandwidth against context length: 128 requests x 1 new token,
+    every request at the same context c, Llama-3-8B shapes."""
+    from ragged_paged_attention_amd.inputs import build_batch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for c in (128, 256, 512, 1024, 2048, 4096, 8192):
+        b = build_batch([1] * 128, [c] * 128, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        seed=2000 + c, name=f"decode_c{c}")
+        dt = [t.to(dev) for t in (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
+                                  b.cu_q_lens, b.context_lens, b.slot_mapping)]
+        call = binding.Prepared(*dt, causal=True, scale=None, variant=args.variant,
+                                cu_q_lens_host=b.cu_q_lens, context_lens_host=b.context_lens)
+        for _ in range(args.warmup):
+            call(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            call(stream)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / args.steps * 1e3
+        timers = [binding.StageTimer() for _ in range(args.steps)]
+        for t in timers:
+            call(stream, t)
+        torch.cuda.synchronize()
+        dec_us = float(np.mean([t.stage_ms()["decode"] for t in timers])) * 1e3
+        for t in timers:
+            t.close()
+        B = algorithmic_bytes(b)
+        print(json.dumps({"sweep": "decode_context", "context": c, "requests": 128,
+                          "step_us": us, "GB_per_s": B / us / 1e3, "frac_of_8TBs": B / us / 1e3 / HBM_PEAK_GBS,
+                          "decode_kernel_us": dec_us, "kernel_GB_per_s": B / dec_us / 1e3,
+                          "algorithmic_bytes": B, "tokens_per_s": 128 / (us * 1e-6)}), flush=True)
+        del call, dt
 
 
 # ---------------------------------------------------------------------------
@@ -253,6 +294,9 @@ def main():
     ap.add_argument("--variant", default="auto", choices=list(binding.VARIANTS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-baseline budget (0 disables the oracle leg)")
+    ap.add_argument("--sweep-decode", action="store_true",
+                    help="instead of the contract line: one JSON line per decode context length "
+                         "(128 requests x 1 token, context 128 .. 8192), HBM fraction against context")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -271,6 +315,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+
+    if args.sweep_decode:
+        sweep_decode(args)
         return
 
     log(f"[bench] building inputs for {args.config}")
@@ -310,6 +358,33 @@ def main():
         t.close()
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step; kernels (us): "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
+
+    # Distribution of single calls (an event pair around each call), and for
+    # a decode-dominated batch the same with a 512 MiB write between calls,
+    # which evicts L2 and the MALL (the cache bytes then all come from HBM).
+    def per_call_us(n, between=None):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            if between is not None:
+                between()
+            e0.record()
+            call(stream)
+            e1.record()
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+
+    def pctl(x):
+        return {"p10": float(np.percentile(x, 10)), "p50": float(np.median(x)),
+                "p90": float(np.percentile(x, 90))}
+
+    single = per_call_us(args.steps)
+    flushed = None
+    if stages["decode"] >= stages["prefill"]:
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fl = per_call_us(args.steps, between=junk.zero_)
+        del junk
+        flushed = {"us": pctl(fl), "GB_per_s_p50": algorithmic_bytes(b) / (np.median(fl) * 1e-6) / 1e9,
+                   "note": "512 MiB written between calls (L2 and MALL evicted)"}
 
     B = algorithmic_bytes(b)
     F = algorithmic_flops(b)
@@ -369,6 +444,8 @@ def main():
         "frac_of_peak_whole_step": frac_step,
         "algorithmic_bytes": B, "algorithmic_flops": F,
         "kernel_us": {k: v * 1e3 for k, v in stages.items()},
+        "step_us_single_calls": pctl(single),
+        "flushed": flushed,
         "roofline": roof,
         "cpu_baseline": cpu,
         "context": {"pages_decode_mbu_tpu7x": 0.86, "pages_prefill_mfu_tpu7x": 0.73,

@@ -88,7 +88,12 @@ typedef struct {
 typedef enum {
     RA_VARIANT_AUTO = 0,
     RA_VARIANT_GENERIC = 1,     /* one simple VALU kernel for every request */
-    RA_VARIANT_SPECIALISED = 2  /* decode kernel + MFMA prefill kernel */
+    RA_VARIANT_SPECIALISED = 2, /* decode kernel + MFMA prefill kernel */
+    RA_VARIANT_UNFUSED = 3      /* ablation of the fusion (the paper's technique of fusing the
+                                   KV-cache update into the kernel): the specialised kernels
+                                   without the update, preceded by a separate scatter kernel;
+                                   same results.  Batches the specialised kernels do not take
+                                   run the generic kernel, fused. */
 } ra_variant;
 
 /*

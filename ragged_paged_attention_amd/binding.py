@@ -17,7 +17,7 @@ _LIB_NAME = "libragged_attn.so"
 
 STATUS = {0: "RA_OK", 1: "RA_E_NULL", 2: "RA_E_SHAPE", 3: "RA_E_UNSUPPORTED",
           4: "RA_E_METADATA", 5: "RA_E_WORKSPACE", 6: "RA_E_HIP"}
-VARIANTS = {"auto": 0, "generic": 1, "specialised": 2}
+VARIANTS = {"auto": 0, "generic": 1, "specialised": 2, "unfused": 3}
 
 
 class RaError(RuntimeError):

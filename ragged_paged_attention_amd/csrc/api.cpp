@@ -148,7 +148,7 @@ ra_status ra_forward_profiled(const ra_shape *s, const void *q, const void *k_ne
     if (st != RA_OK) return st;
     st = check_host_lens(s, cu_h, ctx_h);
     if (st != RA_OK) return st;
-    if (variant < RA_VARIANT_AUTO || variant > RA_VARIANT_SPECIALISED)
+    if (variant < RA_VARIANT_AUTO || variant > RA_VARIANT_UNFUSED)
         return fail(RA_E_SHAPE, "unknown variant %d", variant);
     const bool has_tokens = s->total_tokens > 0;
     if (has_tokens && (!q || !k_new || !v_new || !out || !slot_mapping))
@@ -169,6 +169,7 @@ ra_status ra_forward_profiled(const ra_shape *s, const void *q, const void *k_ne
 
     ra::Params p{};
     p.prefill_only = 0;
+    p.skip_scatter = (variant == RA_VARIANT_UNFUSED && plan.specialised_ok) ? 1 : 0;
     p.q = (const ra::bf16_t *)q;
     p.k_new = (const ra::bf16_t *)k_new;
     p.v_new = (const ra::bf16_t *)v_new;

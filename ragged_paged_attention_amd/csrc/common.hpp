@@ -23,6 +23,7 @@ struct Params {
     int32_t R, T, Hq, Hkv, D, S, max_pages, causal;
     float scale_log2;       // softmax scale * log2(e): scores live in the exp2 domain
     int32_t prefill_only;   // generic kernel: skip tokens of decode (q_r == 1) requests
+    int32_t skip_scatter;   // attention kernels leave the cache alone (a separate scatter ran)
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

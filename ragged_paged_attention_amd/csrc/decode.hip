@@ -399,7 +399,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     // last page, scores/softmax/PV, and the end of the segment.
     auto step = [&](int g, int stage) {
         const int pr = g - cq.pfx;
-        if (g == cq.pend - 1 && lane < CPH) {
+        if (g == cq.pend - 1 && lane < CPH && !p.skip_scatter) {
             // Fused KV-cache update of the new token (position c), this
             // wavefront's kv head: the row is in the LDS tile already (loaded
             // from k_new / v_new), so the copy waits on no global load.

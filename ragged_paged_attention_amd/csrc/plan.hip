@@ -167,6 +167,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     }
 }
 
+// The KV-cache update alone (the unfused ablation): one thread per 16-byte
+// chunk of a new row, K and V.
+__global__ __launch_bounds__(256) void scatter_kernel(Params p) {
+    const int cpr = p.D / 8;
+    const long long n = (long long)p.T * p.Hkv * cpr;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+        const int col = (int)(i % cpr);
+        const long long th = i / cpr;  // token * Hkv + head
+        const int t = (int)(th / p.Hkv), h = (int)(th - (long long)t * p.Hkv);
+        const size_t src = (size_t)th * p.D + 8 * col;
+        const size_t dst = ((size_t)p.slot_mapping[t] * p.Hkv + h) * p.D + 8 * col;
+        *reinterpret_cast<uint4 *>(p.k_cache + dst) = *reinterpret_cast<const uint4 *>(p.k_new + src);
+        *reinterpret_cast<uint4 *>(p.v_cache + dst) = *reinterpret_cast<const uint4 *>(p.v_new + src);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipStream_t stream,
@@ -189,6 +205,15 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     int4 *pre = (int4 *)(w + plan.off_prefill);
     err = ev.record(0);
     if (err != hipSuccess) return err;
+    if (p.skip_scatter) {
+        // Unfused ablation: the cache update runs first as its own kernel
+        // (timed with the plan kernel in the stage events).
+        const long long chunks = (long long)p.T * p.Hkv * (p.D / 8);
+        const int blocks = (int)std::min<long long>((chunks + 255) / 256, 4096);
+        hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, stream, p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
                        p.context_lens, p.R, p.S, plan.q_tile, p.Hkv, dw.nwg,
                        (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,

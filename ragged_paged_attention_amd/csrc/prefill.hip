@@ -185,7 +185,7 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
     const size_t prow = (size_t)r * p.max_pages;
 
     // Fused KV-cache update: the new rows of this tile's tokens, kv head hk.
-    for (int idx = tid; idx < tile_q * CPR; idx += NTHR) {
+    for (int idx = tid; idx < (p.skip_scatter ? 0 : tile_q * CPR); idx += NTHR) {
         const int row = idx / CPR, col = idx - row * CPR;
         const int t = t0 + q0 + row;
         const size_t dst = ((size_t)ld_meta(p.slot_mapping, t) * Hkv + hk) * D + 8 * col;
@@ -625,6 +625,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 
     // Fused KV-cache update, the new rows of this tile's tokens for kv head
     // hk: loaded here with the other prologue loads, stored after them.
+    const int kv_chunks = p.skip_scatter ? 0 : tile_q * CPR;
     // Two 16-byte chunks per thread and tensor cover tile_q <= 64 rows (at
     // head_dim 128; G >= 4); larger tiles copy the rest after the prologue.
     constexpr int KVU = 2;
@@ -633,7 +634,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 #pragma unroll
     for (int i = 0; i < KVU; ++i) {
         const int idx = tid + i * NTHR;
-        if (idx < tile_q * CPR) {
+        if (idx < kv_chunks) {
             const int row = idx / CPR, col = idx - row * CPR;
             const int t = t0 + q0 + row;
             const size_t src = ((size_t)t * Hkv + hk) * D + 8 * col;
@@ -963,14 +964,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 #pragma unroll
     for (int i = 0; i < KVU; ++i) {
         const int idx = tid + i * NTHR;
-        if (idx < tile_q * CPR) {
+        if (idx < kv_chunks) {
             const int col = idx % CPR;
             const size_t dst = ((size_t)kvslot[i] * Hkv + hk) * D + 8 * col;
             *reinterpret_cast<short8_t *>(p.k_cache + dst) = kvk[i];
             *reinterpret_cast<short8_t *>(p.v_cache + dst) = kvv[i];
         }
     }
-    for (int idx = tid + KVU * NTHR; idx < tile_q * CPR; idx += NTHR) {
+    for (int idx = tid + KVU * NTHR; idx < kv_chunks; idx += NTHR) {
         const int row = idx / CPR, col = idx - row * CPR;
         const int t = t0 + q0 + row;
         const size_t dst = ((size_t)p.slot_mapping[t] * Hkv + hk) * D + 8 * col;

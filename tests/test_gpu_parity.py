@@ -272,3 +272,22 @@ def test_profiled_call_reports_stage_times():
     assert set(ms) == set(binding.STAGES)
     assert all(v >= 0 for v in ms.values())
     assert ms["decode"] > 0 and ms["prefill"] > 0
+
+
+@pytest.mark.parametrize("seed,D,G", [(61, 64, 4), (62, 128, 4), (63, 128, 1), (64, 256, 2)])
+def test_unfused_ablation_matches_fused(seed, D, G):
+    """The unfused ablation (separate scatter kernel, attention kernels without
+    the cache update) gives bitwise the fused call's output and caches, and
+    both match the oracle."""
+    hkv = 2
+    b = random_batch(seed, num_reqs=9, max_q=150, max_ctx=700, num_q_heads=hkv * G, num_kv_heads=hkv,
+                     head_dim=D)
+    say(f"[parity] unfused vs fused seed={seed} D={D} G={G} T={b.total_tokens}")
+    o1, k1, v1 = run_gpu(b, "specialised")
+    o2, k2, v2 = run_gpu(b, "unfused")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "outputs differ"
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), "k caches differ"
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16)), "v caches differ"
+    ref, rkc, rvc = oracle_full(b)
+    assert np.array_equal(u16(k2), rkc) and np.array_equal(u16(v2), rvc)
+    assert_close(o2, ref, "unfused")
