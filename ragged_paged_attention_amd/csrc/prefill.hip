@@ -979,7 +979,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
         *reinterpret_cast<uint4 *>(p.k_cache + dst) = *reinterpret_cast<const uint4 *>(p.k_new + src);
         *reinterpret_cast<uint4 *>(p.v_cache + dst) = *reinterpret_cast<const uint4 *>(p.v_new + src);
     }
-    __syncthreads();
+    // The loads above were waited for by every wavefront; the cache stores
+    // need not complete before the loop (a fence here would wait for them).
+    barrier();
     if (grp == 1) barrier();     // group 1 starts one phase late
 
     auto step = [&](auto U, int t) {
