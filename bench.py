@@ -284,6 +284,61 @@ def sweep_decode(args):
         del call, dt
 
 
+def time_call(b: Batch, args):
+    """Mean step time (us) of plain calls, and the per-stage event means."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dt = [t.to(dev) for t in (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
+                              b.cu_q_lens, b.context_lens, b.slot_mapping)]
+    call = binding.Prepared(*dt, causal=b.causal, scale=None, variant=args.variant,
+                            cu_q_lens_host=b.cu_q_lens, context_lens_host=b.context_lens)
+    for _ in range(args.warmup):
+        call(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        call(stream)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / args.steps * 1e3
+    timers = [binding.StageTimer() for _ in range(args.steps)]
+    for t in timers:
+        call(stream, t)
+    torch.cuda.synchronize()
+    stages = {s: float(np.mean([t.stage_ms()[s] for t in timers])) * 1e3 for s in binding.STAGES}
+    for t in timers:
+        t.close()
+    return us, stages
+
+
+def sweep_shapes(args):
+    """head_dim x page_size: a decode batch (128 requests x 1 token, context
+    4096) and a causal prefill batch (4 x 2048 tokens), Hkv = 8, G = 4 at
+    head_dim 64 / 128 and G = 2 at 256."""
+    from ragged_paged_attention_amd.inputs import build_batch
+    for D in (64, 128, 256):
+        hq = 16 if D == 256 else 32
+        for S in (16, 32, 64):
+            dec = build_batch([1] * 128, [4096] * 128, num_q_heads=hq, num_kv_heads=8, head_dim=D,
+                              page_size=S, seed=3000 + D + S, name="decode")
+            us, st = time_call(dec, args)
+            B = algorithmic_bytes(dec)
+            print(json.dumps({"sweep": "shapes", "kind": "decode", "head_dim": D, "page_size": S,
+                              "step_us": us, "GB_per_s": B / us / 1e3, "frac_of_8TBs": B / us / 1e3 / HBM_PEAK_GBS,
+                              "decode_kernel_us": st["decode"]}), flush=True)
+            del dec
+            pre = build_batch([2048] * 4, [0] * 4, num_q_heads=hq, num_kv_heads=8, head_dim=D,
+                              page_size=S, seed=4000 + D + S, name="prefill")
+            us, st = time_call(pre, args)
+            F = algorithmic_flops(pre)
+            print(json.dumps({"sweep": "shapes", "kind": "prefill_causal", "head_dim": D, "page_size": S,
+                              "step_us": us, "TFLOP_per_s": F / us / 1e6,
+                              "frac_of_peak": F / us / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+                              "prefill_kernel_us": st["prefill"]}), flush=True)
+            del pre
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -297,6 +352,9 @@ def main():
     ap.add_argument("--sweep-decode", action="store_true",
                     help="instead of the contract line: one JSON line per decode context length "
                          "(128 requests x 1 token, context 128 .. 8192), HBM fraction against context")
+    ap.add_argument("--sweep-shapes", action="store_true",
+                    help="instead of the contract line: one JSON line per head_dim x page_size "
+                         "(64/128/256 x 16/32/64) for a decode batch and a causal prefill batch")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -319,6 +377,9 @@ def main():
 
     if args.sweep_decode:
         sweep_decode(args)
+        return
+    if args.sweep_shapes:
+        sweep_shapes(args)
         return
 
     log(f"[bench] building inputs for {args.config}")

@@ -36,7 +36,8 @@
  *                page_table[r][(c_r+i)/S] * S + (c_r+i) % S for token i of r
  *   out          [T][Hq][D]             bf16, device, written
  *
- * Supported: D in {64, 128, 256}; S = 16; Hq % Hkv == 0; Hq / Hkv <= 16.
+ * Supported: D in {64, 128, 256}; S a multiple of 16, at most 1024 (the kernels
+ * walk the cache in 16-row blocks of a page); Hq % Hkv == 0; Hq / Hkv <= 16.
  *
  * Ownership and concurrency: the caller owns every buffer, the workspace
  * included; the library allocates no device memory and keeps no state

@@ -43,7 +43,9 @@ ra_status check_shape(const ra_shape *s) {
     const int D = s->head_dim, G = s->num_q_heads / s->num_kv_heads;
     if (!(D == 64 || D == 128 || D == 256))
         return fail(RA_E_UNSUPPORTED, "head_dim %d not supported (64, 128, 256)", D);
-    if (s->page_size != 16) return fail(RA_E_UNSUPPORTED, "page_size %d not supported (16)", s->page_size);
+    if (s->page_size % 16 != 0 || s->page_size > 1024)
+        return fail(RA_E_UNSUPPORTED, "page_size %d not supported (a multiple of 16, at most 1024)",
+                    s->page_size);
     if (G > 16) return fail(RA_E_UNSUPPORTED, "Hq/Hkv = %d above 16", G);
     const long long rows = (long long)s->num_pages * s->page_size * s->num_kv_heads * D;
     if (rows > (1LL << 40)) return fail(RA_E_UNSUPPORTED, "cache too large");

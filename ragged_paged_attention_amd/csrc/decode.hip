@@ -207,8 +207,14 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         while (pid_base >= fq.pend) fq = fetch_req(p, dw, fq.i + 1);
         for (;;) {
             const int sb = max(pid_base, fq.pfx), se = min(ge, fq.pend);
-            const int32_t *row = p.page_table + (size_t)fq.r * p.max_pages + (sb - fq.pfx);
-            for (int x = tid; x < se - sb; x += NTHR) pid_lds[sb - pid_base + x] = row[x];
+            // Entries are 16-row blocks: block k of a request is sub-block
+            // k % (S / 16) of its page k / (S / 16).
+            const int32_t *row = p.page_table + (size_t)fq.r * p.max_pages;
+            const int spb = p.S >> 4;
+            for (int x = tid; x < se - sb; x += NTHR) {
+                const int k = sb - fq.pfx + x;
+                pid_lds[sb - pid_base + x] = row[k / spb] * spb + k % spb;
+            }
             if (fq.pend >= ge) break;
             fq = fetch_req(p, dw, fq.i + 1);
         }

@@ -24,7 +24,7 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
         const int q = cu[r + 1] - cu[r];
         if (q == 1) {
             ++pl.n_decode_reqs;
-            np += ceil_div((long long)ctx[r] + 1, s.page_size);
+            np += ceil_div((long long)ctx[r] + 1, 16);  // 16-row blocks of pages
         } else if (q > 1) {
             ++pl.n_prefill_reqs;
         }
@@ -34,7 +34,7 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     pl.decode_hgroups = Hkv / pl.decode_hw;
     pl.decode_wg_cap = pl.n_decode_reqs ? std::max(1, kMaxDecodeWorkgroups / pl.decode_hgroups) : 0;
     pl.q_tile = prefill_supports(D, G) ? prefill_rows(D) / G : 0;
-    pl.specialised_ok = (s.page_size == 16) && (D == 64 || D == 128 || D == 256) && G <= 16 &&
+    pl.specialised_ok = (s.page_size % 16 == 0) && (D == 64 || D == 128 || D == 256) && G <= 16 &&
                         (pl.n_prefill_reqs == 0 || pl.q_tile > 0);
     for (int r = 0; r < R; ++r) {
         const int q = cu[r + 1] - cu[r];
@@ -215,7 +215,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
-                       p.context_lens, p.R, p.S, plan.q_tile, p.Hkv, dw.nwg,
+                       p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg,
                        (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
                        (int32_t *)(w + plan.off_ppfx), pre);
     err = hipGetLastError();

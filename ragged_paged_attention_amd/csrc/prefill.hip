@@ -240,7 +240,7 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
     auto load_tile = [&](int tile, int stage) {
         const int jw = tile * N + RW * w;                 // first key row of this wavefront
         const int jp = min(jw, kv_end - 1);               // a visible position of the same page
-        const size_t page = (size_t)ld_meta(p.page_table, prow + jp / 16);
+        const size_t page = (size_t)ld_meta(p.page_table, prow + jp / p.S);
         bf16_t *kst = smem + stage * 2 * TILE + RW * w * D;
 #pragma unroll
         for (int u = 0; u < IPW; ++u) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
             const int row = RW * w + kr;                  // row inside the tile
             const int lk = lpc ^ (row & SWM);             // logical K chunk landing at lpc
             const int lv = lpc ^ v_swizzle(row);          // logical V chunk landing at lpc
-            const size_t crow = ((page * 16 + (j & 15)) * Hkv + hk) * D;
+            const size_t crow = ((page * p.S + j % p.S) * Hkv + hk) * D;
             const size_t nrow = ((size_t)(j - c) * Hkv + hk) * D;
             const bool cached = j < c;
             load_lds16((cached ? kcache + crow : knew + nrow) + 8 * lk, kst + RPI * u * D);
@@ -700,9 +700,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
             // base + 32-bit lane offset.
             const char *kb, *vb;
             if (jw < c) {
-                const size_t page = (size_t)ld_meta(p.page_table, prow + jw / 16);
-                kb = (const char *)(kcache + page * 16 * rstride);
-                vb = (const char *)(vcache + page * 16 * rstride);
+                const size_t page = (size_t)ld_meta(p.page_table, prow + jw / p.S);
+                const size_t row0 = page * p.S + jw % p.S;  // 16 | S: the 16 rows share a page
+                kb = (const char *)(kcache + row0 * rstride);
+                vb = (const char *)(vcache + row0 * rstride);
             } else {
                 kb = (const char *)(knew + (size_t)(jw - c) * rstride);
                 vb = (const char *)(vnew + (size_t)(jw - c) * rstride);
@@ -717,14 +718,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
             // visible key: per-lane sources; rows past the end repeat the
             // last visible key (finite, and masked).
             const int jp = min(jw, kv_end - 1);
-            const size_t page = (size_t)ld_meta(p.page_table, prow + jp / 16);
+            const size_t page = (size_t)ld_meta(p.page_table, prow + jp / p.S);
 #pragma unroll
             for (int u = 0; u < IPL; ++u) {
                 const int lr = (int)opaque(lrow);
                 const int kr = RPI * u + lr;
                 const int j = min(jw + kr, kv_end - 1);
                 const uint32_t d_k = lofs_k(u) - 2u * lr * Hkv * D, d_v = bv - 2u * lr * Hkv * D;
-                const size_t crow = (page * 16 + (j & 15)) * rstride;
+                const size_t crow = (page * p.S + j % p.S) * rstride;
                 const size_t nrow = (size_t)(j - c) * rstride;
                 const bool cached = j < c;
                 const char *kr_ = (const char *)(cached ? kcache + crow : knew + nrow);

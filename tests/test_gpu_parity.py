@@ -107,6 +107,28 @@ def test_random_batches(case, variant):
     check_small(b, variant)
 
 
+PAGED = [
+    # (seed, S, R, max_q, max_ctx, Hq, Hkv, D, decode_frac, causal)
+    (31, 32, 6, 70, 300, 32, 8, 128, 0.5, True),
+    (32, 64, 6, 70, 300, 32, 8, 128, 0.5, True),
+    (33, 32, 5, 50, 200, 8, 2, 64, 0.5, True),
+    (34, 64, 4, 40, 500, 16, 8, 256, 0.5, True),
+    (35, 128, 4, 90, 700, 8, 8, 128, 0.4, False),
+    (36, 32, 8, 1, 2000, 32, 8, 128, 1.0, True),   # decode only, several splits
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("case", PAGED, ids=lambda c: f"S{c[1]}-s{c[0]}")
+def test_page_sizes(case, variant):
+    """Pages of 32, 64 and 128 rows: the specialised kernels walk them in
+    16-row blocks; contexts and chunk boundaries fall anywhere inside a page."""
+    seed, S, R, mq, mc, Hq, Hkv, D, frac, causal = case
+    b = random_batch(seed, num_reqs=R, max_q=mq, max_ctx=mc, num_q_heads=Hq, num_kv_heads=Hkv,
+                     head_dim=D, decode_frac=frac, causal=causal, page_size=S)
+    check_small(b, variant)
+
+
 EDGES = {
     # name: (q_lens, ctx_lens, Hq, Hkv, D)
     "page_multiple": ([1, 1, 16], [15, 31, 16], 8, 2, 128),     # L = 16, 32, 32
