@@ -40,10 +40,14 @@
  * walk the cache in 16-row blocks of a page); Hq % Hkv == 0; Hq / Hkv <= 16.
  *
  * Ownership and concurrency: the caller owns every buffer, the workspace
- * included; the library allocates no device memory and keeps no state
+ * included; the library allocates no device memory and keeps no data
  * between calls.  Host pointers are read during the call only.  ra_forward
  * is asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
- * never synchronises.  `out` must not alias any input.  A slot written by
+ * never synchronises.  A batch with both decode and prefill requests runs
+ * its prefill kernel on a second stream beside the decode kernel, forked
+ * from and joined back into `stream` with events (capturable in a graph);
+ * that stream and its two events are created per device on first use and
+ * live until the process ends.  `out` must not alias any input.  A slot written by
  * this call must not be read, as prior context, by any request of the same
  * call.  Two calls that share a workspace must be ordered on one stream.
  *

@@ -1,6 +1,9 @@
 // plan.hip -- host planning, the device plan kernel and the launch sequence
 // of the specialised path.
+#include <stdlib.h>
+
 #include <algorithm>
+#include <mutex>
 
 #include "launch.hpp"
 #include "plan.hpp"
@@ -36,9 +39,23 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     pl.q_tile = prefill_supports(D, G) ? prefill_rows(D) / G : 0;
     pl.specialised_ok = (s.page_size % 16 == 0) && (D == 64 || D == 128 || D == 256) && G <= 16 &&
                         (pl.n_prefill_reqs == 0 || pl.q_tile > 0);
+    double dec_bytes = 0, pre_flops = 0;
     for (int r = 0; r < R; ++r) {
         const int q = cu[r + 1] - cu[r];
         if (q > 1 && pl.q_tile > 0) pl.n_prefill_items += (int)ceil_div(q, pl.q_tile) * Hkv;
+        if (q == 1) dec_bytes += (double)(ctx[r] + 1) * Hkv * D * 4;
+        if (q > 1) {
+            const double c = ctx[r];
+            const double pairs = s.causal ? q * c + 0.5 * q * (q + 1.0) : (double)q * (c + q);
+            pre_flops += pairs * s.num_q_heads * 4.0 * D;
+        }
+    }
+    // Share of the compute units the decode kernel starts on when a mixed
+    // batch runs its prefill kernel beside it: the decode part of the two
+    // estimated times (about 6.5 TB/s and 750 TFLOP/s), within [0.4, 0.9].
+    if (dec_bytes > 0 && pre_flops > 0) {
+        const double td = dec_bytes / 6.5e12, tp = pre_flops / 7.5e14;
+        pl.decode_share_pm = (int)(1000 * std::min(0.9, std::max(0.4, td / (td + tp))));
     }
     const int nd = pl.n_decode_reqs, nhg = pl.decode_hgroups, cap = pl.decode_wg_cap;
     const size_t slots = (size_t)nhg * cap * 2;  // two partial slots per workgroup
@@ -183,6 +200,40 @@ __global__ __launch_bounds__(256) void scatter_kernel(Params p) {
     }
 }
 
+// Concurrent mixed batches: the prefill kernel runs on a second stream next
+// to the decode kernel (MFMA-bound and HBM-bound work on different compute
+// units).  One side stream and two fork/join events per device, created on
+// first use and kept until the process ends; a mutex keeps the record / wait
+// sequence of concurrent callers apart.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+hipError_t side_stream(SideStream **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    SideStream &ss = g_side[dev];
+    if (!ss.s) {
+        e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+    }
+    *out = &ss;
+    return hipSuccess;
+}
+
+int env_int(const char *name, int dflt) {
+    const char *v = getenv(name);
+    return v ? atoi(v) : dflt;
+}
+
 }  // namespace
 
 hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipStream_t stream,
@@ -198,9 +249,18 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
     hipError_t err = hipSuccess;
+    // A batch with both kinds of work runs its prefill kernel beside the
+    // decode kernel (not when the caller times the stages), and the decode
+    // kernel then leaves a quarter of the compute units to it at first.
+    const bool overlap = !ev.events && dw.nd > 0 && plan.n_prefill_items > 0 &&
+                         env_int("RA_MIXED_OVERLAP", 1) != 0;
     if (dw.nd > 0) {
         err = decode_workgroups(p, plan, &dw.nwg);
         if (err != hipSuccess) return err;
+        if (overlap) {
+            const int per_mille = env_int("RA_MIXED_DECODE_SHARE", plan.decode_share_pm);
+            dw.nwg = std::max(1, std::min(dw.nwg, (int)((long long)dw.nwg * per_mille / 1000)));
+        }
     }
     int4 *pre = (int4 *)(w + plan.off_prefill);
     err = ev.record(0);
@@ -219,7 +279,22 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
                        (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
                        (int32_t *)(w + plan.off_ppfx), pre);
     err = hipGetLastError();
-    if (err == hipSuccess) err = ev.record(1);
+    if (err != hipSuccess) return err;
+    if (overlap) {
+        SideStream *ss = nullptr;
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        err = side_stream(&ss);
+        // The decode kernel is queued first so that its (persistent)
+        // workgroups take their compute units before the prefill items do.
+        if (err == hipSuccess) err = hipEventRecord(ss->fork, stream);
+        if (err == hipSuccess) err = launch_decode(p, dw, stream, ev);
+        if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
+        if (err == hipSuccess) err = launch_prefill(p, plan, pre, ss->s);
+        if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
+        if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
+        return err;
+    }
+    err = ev.record(1);
     if (err == hipSuccess && plan.n_prefill_items > 0) err = launch_prefill(p, plan, pre, stream);
     if (err == hipSuccess) err = ev.record(2);
     if (err == hipSuccess) {

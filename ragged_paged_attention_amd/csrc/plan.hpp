@@ -45,6 +45,7 @@ struct Plan {
     // prefill
     int q_tile = 0;             // query tokens per prefill work item
     int n_prefill_items = 0;    // (request, kv head, query tile) triples
+    int decode_share_pm = 1000; // mixed batches: per mille of the decode grid launched beside prefill
     // which path runs
     bool specialised_ok = false;
     // workspace layout (byte offsets, 256-aligned)
