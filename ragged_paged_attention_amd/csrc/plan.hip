@@ -33,7 +33,7 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
         }
     }
     pl.n_decode_pages = (int)np;
-    pl.decode_hw = decode_heads_per_group(D, Hkv);
+    pl.decode_hw = decode_heads_per_group(D, Hkv, np, pl.n_decode_reqs);
     pl.decode_hgroups = Hkv / pl.decode_hw;
     pl.decode_wg_cap = pl.n_decode_reqs ? std::max(1, kMaxDecodeWorkgroups / pl.decode_hgroups) : 0;
     pl.q_tile = prefill_supports(D, G) ? prefill_rows(D) / G : 0;
@@ -57,19 +57,27 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
         const double td = dec_bytes / 6.5e12, tp = pre_flops / 7.5e14;
         pl.decode_share_pm = (int)(1000 * std::min(0.9, std::max(0.4, td / (td + tp))));
     }
-    const int nd = pl.n_decode_reqs, nhg = pl.decode_hgroups, cap = pl.decode_wg_cap;
-    const size_t slots = (size_t)nhg * cap * 2;  // two partial slots per workgroup
+    const int nd = pl.n_decode_reqs;
+    // Two partial slots per workgroup, (kv heads of the group) x G q heads
+    // each.  The slots and the workgroup table are sized for the larger of
+    // the chosen head-group size and the long-context one, so that the
+    // workspace does not depend on the context lengths.
+    const int hw_long = decode_heads_per_group(D, Hkv, 0, 0);
+    auto wg_cap = [&](int hw) { return std::max(1, kMaxDecodeWorkgroups / (Hkv / hw)); };
+    auto slot_heads = [&](int hw) { return (size_t)(Hkv / hw) * wg_cap(hw) * 2 * hw * G; };
+    const size_t part_heads = std::max(slot_heads(pl.decode_hw), slot_heads(hw_long));
+    const int cap_max = std::max(wg_cap(pl.decode_hw), wg_cap(hw_long));
     size_t off = 0;
     pl.off_dreq = off;
     off = align256(off + sizeof(int32_t) * (size_t)nd);
     pl.off_dpfx = off;
     off = align256(off + sizeof(int32_t) * ((size_t)nd + 1));
     pl.off_wstart = off;
-    off = align256(off + sizeof(int32_t) * (size_t)cap);
+    off = align256(off + sizeof(int32_t) * (size_t)(nd ? cap_max : 0));
     pl.off_part_o = off;
-    off = align256(off + sizeof(float) * (nd ? slots * pl.decode_hw * G * D : 0));
+    off = align256(off + sizeof(float) * (nd ? part_heads * D : 0));
     pl.off_part_ml = off;
-    off = align256(off + sizeof(float) * (nd ? slots * pl.decode_hw * G * 2 : 0));
+    off = align256(off + sizeof(float) * (nd ? part_heads * 2 : 0));
     pl.off_ppfx = off;
     off = align256(off + sizeof(int32_t) * ((size_t)R + 1));
     pl.off_prefill = off;
@@ -248,6 +256,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.nd = plan.n_decode_reqs;
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
+    dw.hw = plan.decode_hw;
     hipError_t err = hipSuccess;
     // A batch with both kinds of work runs its prefill kernel beside the
     // decode kernel (not when the caller times the stages), and the decode

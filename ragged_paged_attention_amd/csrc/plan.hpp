@@ -63,6 +63,7 @@ struct DecodeWork {
     float *part_o;          // [nhg][nwg][2][HW*G][D] partial o (unnormalised)
     float *part_ml;         // [nhg][nwg][2][HW*G][2] partial (m, l)
     int nd, np, nwg;        // decode requests, flat pages, workgroups per head group
+    int hw;                 // kv heads per workgroup
 };
 
 // Optional hipEvents recorded at the stage boundaries of one call.
@@ -82,8 +83,9 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
                        const StageEvents &ev);
 
 // Kernels of the specialised path.
-// kv heads per decode workgroup for this head_dim and kv-head count.
-int decode_heads_per_group(int D, int Hkv);
+// kv heads per decode workgroup for this head_dim, kv-head count and batch
+// (blocks: 16-row page blocks of all nd decode requests).
+int decode_heads_per_group(int D, int Hkv, long long blocks, int nd);
 // Decode workgroups per head group to launch on the current device.
 hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg);
 // Launches the decode kernel, records event 3, launches the merge kernel.
