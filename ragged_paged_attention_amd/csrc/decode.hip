@@ -132,15 +132,70 @@ __device__ __forceinline__ int ld_meta(const int32_t *a, size_t i) {
     return ((const __attribute__((address_space(4))) int32_t *)a)[i];
 }
 
-__device__ __forceinline__ DecodeReq fetch_req(const Params &p, const DecodeWork &dw, int i) {
+// 16-row blocks of a decode request with c prior tokens (c + 1 keys).
+__device__ __forceinline__ int blocks_of(int c) { return (c + 16) >> 4; }
+
+// Decode request i of the list, whose first flat page is pfx.
+__device__ __forceinline__ DecodeReq make_req(const Params &p, const DecodeWork &dw, int i, int pfx) {
     DecodeReq q;
     q.i = i;
-    q.r = ld_meta(dw.dreq, i);
-    q.pfx = ld_meta(dw.dpfx, i);
-    q.pend = ld_meta(dw.dpfx, i + 1);
+    q.r = dw.self_plan ? i : ld_meta(dw.dreq, i);
     q.t0 = ld_meta(p.cu_q_lens, q.r);
     q.c = ld_meta(p.context_lens, q.r);
+    q.pfx = pfx;
+    q.pend = pfx + blocks_of(q.c);
     return q;
+}
+
+// The decode request after q.
+__device__ __forceinline__ DecodeReq next_req(const Params &p, const DecodeWork &dw, const DecodeReq &q) {
+    return make_req(p, dw, q.i + 1, q.pend);
+}
+
+// Batches whose requests are all decode requests (at most kSelfPlanReqs of
+// them) need no plan kernel: every wavefront finds the request holding its
+// workgroup's first flat page g0 itself, from the prefix sums of the
+// requests' block counts (lane l holds requests l, l + 64, ...: one round
+// trip of loads, then a wave scan per 64 requests), and wavefront 0 of head
+// group 0 writes the list entries of the requests that start inside
+// [g0, g1) for the merge kernel.  Returns {request, its first flat page}.
+__device__ __forceinline__ int2 self_plan_first(const Params &p, const DecodeWork &dw, int g0, int g1,
+                                                bool write_list) {
+    constexpr int KR = kSelfPlanReqs / 64;
+    const int lane = threadIdx.x & 63, R = p.R;
+    int nb[KR];
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        const int r = 64 * k + lane;
+        nb[k] = r < R ? blocks_of(p.context_lens[r]) : 0;
+    }
+    int base = 0, first = -1, first_pfx = 0;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        if (64 * k >= R) break;
+        int incl = nb[k];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
+        }
+        const int r = 64 * k + lane;
+        const int excl = base + incl - nb[k];
+        if (write_list && r < R && excl >= g0 && excl < g1) {
+            const_cast<int32_t *>(dw.dpfx)[r] = excl;
+            const_cast<int32_t *>(dw.dreq)[r] = r;
+        }
+        if (first < 0) {
+            const unsigned long long hit = __builtin_amdgcn_ballot_w64(r < R && base + incl > g0);
+            if (hit) {
+                const int ln = __builtin_ctzll(hit);
+                first = 64 * k + ln;
+                first_pfx = __shfl(excl, ln, 64);
+            }
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    return make_int2(__builtin_amdgcn_readfirstlane(first), __builtin_amdgcn_readfirstlane(first_pfx));
 }
 
 // Workgroup holding flat page g when NP pages are cut into nwg equal ranges
@@ -199,12 +254,20 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     // LDS in one cooperative pass (a scalar walk over the requests they
     // belong to), so that the page loop never waits on a memory round trip
     // for an id --------------------------------------------------------------
-    const int first = ld_meta(dw.wstart, b);
-    DecodeReq fq = fetch_req(p, dw, first);  // fill cursor
+    DecodeReq first_q;
+    if (dw.self_plan) {
+        const int2 f = self_plan_first(p, dw, g0, g1, hg == 0 && w == 0);
+        if (hg == 0 && tid == 0 && g1 == np) const_cast<int32_t *>(dw.dpfx)[dw.nd] = np;
+        first_q = make_req(p, dw, f.x, f.y);
+    } else {
+        const int first = ld_meta(dw.wstart, b);
+        first_q = make_req(p, dw, first, ld_meta(dw.dpfx, first));
+    }
+    DecodeReq fq = first_q;  // fill cursor
     int pid_base = g0;                       // flat page held in pid_lds[0]
     auto fill_pids = [&]() {
         const int ge = min(pid_base + kNumPids, g1);
-        while (pid_base >= fq.pend) fq = fetch_req(p, dw, fq.i + 1);
+        while (pid_base >= fq.pend) fq = next_req(p, dw, fq);
         for (;;) {
             const int sb = max(pid_base, fq.pfx), se = min(ge, fq.pend);
             // Entries are 16-row blocks: block k of a request is sub-block
@@ -216,14 +279,14 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
                 pid_lds[sb - pid_base + x] = row[k / spb] * spb + k % spb;
             }
             if (fq.pend >= ge) break;
-            fq = fetch_req(p, dw, fq.i + 1);
+            fq = next_req(p, dw, fq);
         }
         __syncthreads();
     };
     fill_pids();
 
     // ---- load cursor: walks the flat pages g0.. in order, PF ahead ---------
-    DecodeReq lq = fetch_req(p, dw, first);
+    DecodeReq lq = first_q;
     // Pages past the workgroup's range (the ring's last PF loads) read the
     // new-token rows of the current request instead: the instruction stream
     // stays the same on every path, so the compiler's wait counts stay exact
@@ -239,7 +302,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
                 pid_base += kNumPids;
                 fill_pids();
             }
-            while (g >= lq.pend) lq = fetch_req(p, dw, lq.i + 1);
+            while (g >= lq.pend) lq = next_req(p, dw, lq);
             pr = g - lq.pfx;  // page index inside the request
             pid = (size_t)__builtin_amdgcn_readfirstlane(pid_lds[g - pid_base]);
         }
@@ -421,7 +484,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         if (g == cq.pend - 1 || g == g1 - 1) {
             finish_segment(g);
             if (g + 1 < g1) {
-                cq = fetch_req(p, dw, cq.i + 1);
+                cq = next_req(p, dw, cq);
                 seg_g = g + 1;
                 load_q();
 #pragma unroll

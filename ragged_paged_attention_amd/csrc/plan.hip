@@ -257,6 +257,9 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
     dw.hw = plan.decode_hw;
+    // Decode-only batches (every request one new token) skip the plan kernel.
+    dw.self_plan = (plan.n_prefill_reqs == 0 && dw.nd == p.R && p.R <= kSelfPlanReqs &&
+                    env_int("RA_SELF_PLAN", 1) != 0) ? 1 : 0;
     hipError_t err = hipSuccess;
     // A batch with both kinds of work runs its prefill kernel beside the
     // decode kernel (not when the caller times the stages), and the decode
@@ -283,12 +286,14 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
-                       p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg,
-                       (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
-                       (int32_t *)(w + plan.off_ppfx), pre);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (!dw.self_plan) {
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
+                           p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg,
+                           (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
+                           (int32_t *)(w + plan.off_ppfx), pre);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     if (overlap) {
         SideStream *ss = nullptr;
         std::lock_guard<std::mutex> lock(g_side_mu);

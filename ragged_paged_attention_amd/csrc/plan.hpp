@@ -30,6 +30,10 @@
 
 namespace ra {
 
+// Largest batch of decode requests whose decode kernel plans its own start
+// (a wave scan over the requests; larger or mixed batches run the plan kernel).
+constexpr int kSelfPlanReqs = 512;
+
 // Upper bound of decode workgroups per call (all head groups together); it
 // sizes the partial-result slots of the workspace independently of the GPU.
 constexpr int kMaxDecodeWorkgroups = 512;
@@ -64,6 +68,9 @@ struct DecodeWork {
     float *part_ml;         // [nhg][nwg][2][HW*G][2] partial (m, l)
     int nd, np, nwg;        // decode requests, flat pages, workgroups per head group
     int hw;                 // kv heads per workgroup
+    int self_plan;          // 1: every request is a decode request, dreq is the identity and
+                            // the decode kernel finds its own start (no plan kernel); it then
+                            // writes dreq / dpfx for the merge kernel
 };
 
 // Optional hipEvents recorded at the stage boundaries of one call.

@@ -144,6 +144,12 @@ EDGES = {
     "many_short_decodes": ([1] * 40, [(7 * i) % 45 for i in range(39)] + [3000], 32, 8, 128),
     "short_decodes_d256": ([1] * 24, [(5 * i) % 33 for i in range(23)] + [1500], 16, 8, 256),
     "short_decodes_g1": ([1] * 30, [(3 * i) % 50 for i in range(30)], 4, 4, 64),
+    # decode-only batches plan their own start in the decode kernel up to 512
+    # requests; past that, or with requests that bring no token, the plan
+    # kernel runs
+    "decode_only_512": ([1] * 512, [(29 * i) % 300 for i in range(512)], 8, 2, 64),
+    "decode_only_513": ([1] * 513, [(29 * i) % 300 for i in range(513)], 8, 2, 64),
+    "decode_and_empty": ([1, 0, 1, 1, 0, 1], [3000, 50, 2000, 16, 7, 1200], 32, 8, 128),
     # more requests than the plan kernel keeps in LDS (its searches then run
     # over global memory), decode and prefill mixed
     "many_requests": ([1 if i % 7 else 3 for i in range(4500)], [(11 * i) % 37 for i in range(4500)],
@@ -169,6 +175,23 @@ def test_decode_with_few_workgroups(wgs, monkeypatch):
     b = build_batch([1] * len(ctx), ctx, num_q_heads=16, num_kv_heads=8, head_dim=128, seed=77,
                     name=f"few_wgs_{wgs}")
     check_small(b, "specialised")
+
+
+def test_self_planned_decode_matches_plan_kernel(monkeypatch):
+    """A decode-only batch finds its work split inside the decode kernel; with
+    the plan kernel forced instead (RA_SELF_PLAN=0) the split, and so every
+    output bit, is the same."""
+    ctx = [5000, 3, 1700, 16, 31, 4096, 900, 0, 2500, 7000, 64]
+    b = build_batch([1] * len(ctx), ctx, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=78,
+                    name="self_plan")
+    out_self, kc_self, _ = run_gpu(b)
+    monkeypatch.setenv("RA_SELF_PLAN", "0")
+    out_plan, kc_plan, _ = run_gpu(b)
+    assert torch.equal(out_self.view(torch.int16), out_plan.view(torch.int16))
+    # bit patterns: unused cache slots hold the NaN sentinel
+    assert torch.equal(kc_self.view(torch.int16), kc_plan.view(torch.int16))
+    ref, _, _ = oracle_full(b)
+    assert_close(out_self, ref, "self_plan")
 
 
 def test_fresh_decode_returns_v_new():
