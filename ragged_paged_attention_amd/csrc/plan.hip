@@ -257,9 +257,12 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
     dw.hw = plan.decode_hw;
-    // Decode-only batches (every request one new token) skip the plan kernel.
-    dw.self_plan = (plan.n_prefill_reqs == 0 && dw.nd == p.R && p.R <= kSelfPlanReqs &&
-                    env_int("RA_SELF_PLAN", 1) != 0) ? 1 : 0;
+    // Batches of one kind (every request one new token, or none with one new
+    // token) skip the plan kernel: the decode or prefill kernel finds its
+    // own work.
+    const bool self_plan = p.R <= kSelfPlanReqs && env_int("RA_SELF_PLAN", 1) != 0;
+    dw.self_plan = (self_plan && plan.n_prefill_reqs == 0 && dw.nd == p.R) ? 1 : 0;
+    const bool prefill_self = self_plan && plan.n_decode_reqs == 0 && plan.n_prefill_items > 0;
     hipError_t err = hipSuccess;
     // A batch with both kinds of work runs its prefill kernel beside the
     // decode kernel (not when the caller times the stages), and the decode
@@ -286,7 +289,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (!dw.self_plan) {
+    if (!dw.self_plan && !prefill_self) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
                            p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg,
                            (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
@@ -303,13 +306,13 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         if (err == hipSuccess) err = hipEventRecord(ss->fork, stream);
         if (err == hipSuccess) err = launch_decode(p, dw, stream, ev);
         if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
-        if (err == hipSuccess) err = launch_prefill(p, plan, pre, ss->s);
+        if (err == hipSuccess) err = launch_prefill(p, plan, pre, false, ss->s);
         if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
         if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
         return err;
     }
     err = ev.record(1);
-    if (err == hipSuccess && plan.n_prefill_items > 0) err = launch_prefill(p, plan, pre, stream);
+    if (err == hipSuccess && plan.n_prefill_items > 0) err = launch_prefill(p, plan, pre, prefill_self, stream);
     if (err == hipSuccess) err = ev.record(2);
     if (err == hipSuccess) {
         if (dw.nd > 0) {

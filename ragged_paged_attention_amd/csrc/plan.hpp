@@ -30,9 +30,57 @@
 
 namespace ra {
 
-// Largest batch of decode requests whose decode kernel plans its own start
-// (a wave scan over the requests; larger or mixed batches run the plan kernel).
+// Largest batch whose decode kernel (decode requests only) or prefill kernel
+// (no decode requests) finds its own work with a wave scan over the
+// requests; larger and mixed batches run the plan kernel.
 constexpr int kSelfPlanReqs = 512;
+
+// Prefill item k of a batch without decode requests (at most kSelfPlanReqs
+// requests), found without the plan kernel: the item the plan kernel would
+// write at position k (requests in order; per request its query tiles,
+// longest key range first, each for every kv head).  Every lane of the
+// calling wavefront must take part: lane l holds requests l, l + 64, ...
+// (one round trip of loads) and a wave scan of their item counts finds the
+// request of item k.
+__device__ __forceinline__ void self_plan_prefill_item(const Params &p, int k, int q_tile, int4 &it,
+                                                       int4 &it2) {
+    constexpr int KR = kSelfPlanReqs / 64;
+    const int lane = threadIdx.x & 63, R = p.R;
+    int q[KR];
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+        const int r = 64 * j + lane;
+        q[j] = r < R ? p.cu_q_lens[r + 1] - p.cu_q_lens[r] : 0;
+    }
+    int base = 0, hit_r = 0, hit_excl = 0;
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+        if (64 * j >= R) break;
+        const int r = 64 * j + lane;
+        const int n = q[j] > 1 ? (q[j] + q_tile - 1) / q_tile * p.Hkv : 0;
+        int incl = n;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
+        }
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(r < R && base + incl > k);
+        if (hit) {
+            const int ln = __builtin_ctzll(hit);
+            hit_r = 64 * j + ln;
+            hit_excl = __shfl(base + incl - n, ln, 64);
+            break;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    const int r = __builtin_amdgcn_readfirstlane(hit_r);
+    const int local = k - __builtin_amdgcn_readfirstlane(hit_excl);
+    const int t0 = p.cu_q_lens[r], qr = p.cu_q_lens[r + 1] - t0;
+    const int ntiles = (qr + q_tile - 1) / q_tile;
+    const int rank = local / p.Hkv, hk = local - rank * p.Hkv;
+    it = make_int4(r, hk, (ntiles - 1 - rank) * q_tile, t0);
+    it2 = make_int4(p.context_lens[r], qr, 0, 0);
+}
 
 // Upper bound of decode workgroups per call (all head groups together); it
 // sizes the partial-result slots of the workspace independently of the GPU.
@@ -98,7 +146,9 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg);
 // Launches the decode kernel, records event 3, launches the merge kernel.
 hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream,
                          const StageEvents &ev);
-hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items,
+// items: the plan kernel's list, or null when the kernel finds its own
+// items (self_plan_prefill_item; batches without decode requests).
+hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
                           hipStream_t stream);
 bool prefill_supports(int D, int G);
 // Query rows (heads x tokens) of one prefill workgroup for this head_dim.

@@ -159,7 +159,7 @@ struct PrefillCfg {
 
 template <int D>
 __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefill_kernel(
-    Params p, const int4 *__restrict__ items) {
+    Params p, const int4 *__restrict__ items, int self_plan, int q_tile) {
     using C = PrefillCfg<D>;
     constexpr int NH = C::NH, ROWS = C::ROWS, N = C::N, KB = C::KB, KS = C::KS, MD = C::MD,
                   CPR = C::CPR, SWM = C::SWM, TILE = C::TILE, NSTAGE = C::NSTAGE, RW = C::RW,
@@ -168,7 +168,13 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
     // smem: NSTAGE stages of [K tile | V tile], each tile N rows x D, swizzled
 
-    const int4 it = items[2 * blockIdx.x], it2 = items[2 * blockIdx.x + 1];
+    int4 it, it2;
+    if (self_plan) {
+        self_plan_prefill_item(p, blockIdx.x, q_tile, it, it2);
+    } else {
+        it = items[2 * blockIdx.x];
+        it2 = items[2 * blockIdx.x + 1];
+    }
     const int r = it.x;
     if (r < 0) return;
     const int hk = it.y, q0 = it.z, t0 = it.w, c = it2.x, qlen = it2.y;
@@ -582,7 +588,8 @@ struct PingPongCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4 *__restrict__ items) {
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4 *__restrict__ items, int self_plan,
+                                                            int q_tile) {
     using C = PingPongCfg<D>;
     constexpr int ROWS = C::ROWS, N = C::N, KB = C::KB, KS = C::KS, MD = C::MD, CPR = C::CPR,
                   SWM = C::SWM, VSS = C::VSS, TILE = C::TILE, RPI = C::RPI, IPL = C::IPL,
@@ -608,7 +615,13 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 
     // The item carries everything the prologue needs, so that every load of
     // the prologue (new K/V rows, Q, the first two tiles) goes out at once.
-    const int4 it = items[2 * blockIdx.x], it2 = items[2 * blockIdx.x + 1];
+    int4 it, it2;
+    if (self_plan) {
+        self_plan_prefill_item(p, blockIdx.x, q_tile, it, it2);
+    } else {
+        it = items[2 * blockIdx.x];
+        it2 = items[2 * blockIdx.x + 1];
+    }
     const int r = it.x;
     if (r < 0) return;
     const int hk = it.y, q0 = it.z, t0 = it.w, c = it2.x, qlen = it2.y;
@@ -1022,10 +1035,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 }
 
 template <int D>
-hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items, hipStream_t stream) {
+hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
+                            hipStream_t stream) {
     if constexpr (D <= 128 && RA_PREFILL_PINGPONG) {
         hipLaunchKernelGGL(prefill_pp_kernel<D>, dim3(plan.n_prefill_items), dim3(PingPongCfg<D>::NTHR), 0,
-                           stream, p, items);
+                           stream, p, items, self_plan ? 1 : 0, plan.q_tile);
         return hipGetLastError();
     }
     using C = PrefillCfg<D>;
@@ -1037,7 +1051,8 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
         configured = true;
     }
     const size_t lds = C::LDS_BYTES;
-    hipLaunchKernelGGL(prefill_kernel<D>, dim3(plan.n_prefill_items), dim3(C::NTHR), lds, stream, p, items);
+    hipLaunchKernelGGL(prefill_kernel<D>, dim3(plan.n_prefill_items), dim3(C::NTHR), lds, stream, p, items,
+                       self_plan ? 1 : 0, plan.q_tile);
     return hipGetLastError();
 }
 
@@ -1056,11 +1071,12 @@ int prefill_rows(int D) {
     }
 }
 
-hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, hipStream_t stream) {
+hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
+                          hipStream_t stream) {
     switch (p.D) {
-        case 64: return launch_prefill_d<64>(p, plan, items, stream);
-        case 128: return launch_prefill_d<128>(p, plan, items, stream);
-        case 256: return launch_prefill_d<256>(p, plan, items, stream);
+        case 64: return launch_prefill_d<64>(p, plan, items, self_plan, stream);
+        case 128: return launch_prefill_d<128>(p, plan, items, self_plan, stream);
+        case 256: return launch_prefill_d<256>(p, plan, items, self_plan, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -150,6 +150,10 @@ EDGES = {
     "decode_only_512": ([1] * 512, [(29 * i) % 300 for i in range(512)], 8, 2, 64),
     "decode_only_513": ([1] * 513, [(29 * i) % 300 for i in range(513)], 8, 2, 64),
     "decode_and_empty": ([1, 0, 1, 1, 0, 1], [3000, 50, 2000, 16, 7, 1200], 32, 8, 128),
+    # prefill-only batches likewise find their items in the prefill kernel
+    "prefill_only_512": ([2 + (i % 5) for i in range(512)], [(13 * i) % 40 for i in range(512)], 8, 2, 64),
+    "prefill_only_513": ([2 + (i % 5) for i in range(513)], [(13 * i) % 40 for i in range(513)], 8, 2, 64),
+    "prefill_and_empty": ([0, 3, 0, 70, 2, 0], [5, 7, 0, 40, 300, 9], 32, 8, 128),
     # more requests than the plan kernel keeps in LDS (its searches then run
     # over global memory), decode and prefill mixed
     "many_requests": ([1 if i % 7 else 3 for i in range(4500)], [(11 * i) % 37 for i in range(4500)],
@@ -192,6 +196,22 @@ def test_self_planned_decode_matches_plan_kernel(monkeypatch):
     assert torch.equal(kc_self.view(torch.int16), kc_plan.view(torch.int16))
     ref, _, _ = oracle_full(b)
     assert_close(out_self, ref, "self_plan")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_self_planned_prefill_matches_plan_kernel(D, monkeypatch):
+    """A prefill-only batch finds its items inside the prefill kernel; the
+    plan kernel's items (RA_SELF_PLAN=0) give the same bits."""
+    q = [300, 2, 0, 129, 64, 1000]
+    c = [0, 50, 7, 200, 1, 3000]
+    b = build_batch(q, c, num_q_heads=16, num_kv_heads=8, head_dim=D, seed=79 + D, name="self_plan_pre")
+    out_self, kc_self, _ = run_gpu(b)
+    monkeypatch.setenv("RA_SELF_PLAN", "0")
+    out_plan, kc_plan, _ = run_gpu(b)
+    assert torch.equal(out_self.view(torch.int16), out_plan.view(torch.int16))
+    assert torch.equal(kc_self.view(torch.int16), kc_plan.view(torch.int16))
+    ref, _, _ = oracle_full(b)
+    assert_close(out_self, ref, "self_plan_pre")
 
 
 def test_fresh_decode_returns_v_new():
