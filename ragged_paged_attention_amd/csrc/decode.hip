@@ -135,15 +135,18 @@ __device__ __forceinline__ int ld_meta(const int32_t *a, size_t i) {
 // 16-row blocks of a decode request with c prior tokens (c + 1 keys).
 __device__ __forceinline__ int blocks_of(int c) { return (c + 16) >> 4; }
 
-// Decode request i of the list, whose first flat page is pfx.
+// Decode request i of the list, whose first flat page is pfx.  Without a
+// plan kernel the list is every request of the batch, and those that are
+// not decode requests hold no pages (the walks step over them).
 __device__ __forceinline__ DecodeReq make_req(const Params &p, const DecodeWork &dw, int i, int pfx) {
     DecodeReq q;
     q.i = i;
     q.r = dw.self_plan ? i : ld_meta(dw.dreq, i);
     q.t0 = ld_meta(p.cu_q_lens, q.r);
     q.c = ld_meta(p.context_lens, q.r);
+    const bool decode = !dw.self_plan || ld_meta(p.cu_q_lens, q.r + 1) - q.t0 == 1;
     q.pfx = pfx;
-    q.pend = pfx + blocks_of(q.c);
+    q.pend = pfx + (decode ? blocks_of(q.c) : 0);
     return q;
 }
 
@@ -152,13 +155,14 @@ __device__ __forceinline__ DecodeReq next_req(const Params &p, const DecodeWork 
     return make_req(p, dw, q.i + 1, q.pend);
 }
 
-// Batches whose requests are all decode requests (at most kSelfPlanReqs of
-// them) need no plan kernel: every wavefront finds the request holding its
-// workgroup's first flat page g0 itself, from the prefix sums of the
-// requests' block counts (lane l holds requests l, l + 64, ...: one round
-// trip of loads, then a wave scan per 64 requests), and wavefront 0 of head
-// group 0 writes the list entries of the requests that start inside
-// [g0, g1) for the merge kernel.  Returns {request, its first flat page}.
+// Batches of at most kSelfPlanReqs requests need no plan kernel: every
+// wavefront finds the request holding its workgroup's first flat page g0
+// itself, from the prefix sums of the requests' block counts (zero for
+// requests that are not decode requests; lane l holds requests l, l + 64,
+// ...: one round trip of loads, then a wave scan per 64 requests), and
+// wavefront 0 of head group 0 writes the first flat page of the decode
+// requests that start inside [g0, g1) for the merge kernel.  Returns
+// {request, its first flat page}.
 __device__ __forceinline__ int2 self_plan_first(const Params &p, const DecodeWork &dw, int g0, int g1,
                                                 bool write_list) {
     constexpr int KR = kSelfPlanReqs / 64;
@@ -167,7 +171,8 @@ __device__ __forceinline__ int2 self_plan_first(const Params &p, const DecodeWor
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
         const int r = 64 * k + lane;
-        nb[k] = r < R ? blocks_of(p.context_lens[r]) : 0;
+        const bool decode = r < R && p.cu_q_lens[r + 1] - p.cu_q_lens[r] == 1;
+        nb[k] = decode ? blocks_of(p.context_lens[r]) : 0;
     }
     int base = 0, first = -1, first_pfx = 0;
 #pragma unroll
@@ -181,10 +186,7 @@ __device__ __forceinline__ int2 self_plan_first(const Params &p, const DecodeWor
         }
         const int r = 64 * k + lane;
         const int excl = base + incl - nb[k];
-        if (write_list && r < R && excl >= g0 && excl < g1) {
-            const_cast<int32_t *>(dw.dpfx)[r] = excl;
-            const_cast<int32_t *>(dw.dreq)[r] = r;
-        }
+        if (write_list && nb[k] > 0 && excl >= g0 && excl < g1) const_cast<int32_t *>(dw.dpfx)[r] = excl;
         if (first < 0) {
             const unsigned long long hit = __builtin_amdgcn_ballot_w64(r < R && base + incl > g0);
             if (hit) {
@@ -257,7 +259,6 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     DecodeReq first_q;
     if (dw.self_plan) {
         const int2 f = self_plan_first(p, dw, g0, g1, hg == 0 && w == 0);
-        if (hg == 0 && tid == 0 && g1 == np) const_cast<int32_t *>(dw.dpfx)[dw.nd] = np;
         first_q = make_req(p, dw, f.x, f.y);
     } else {
         const int first = ld_meta(dw.wstart, b);
@@ -484,7 +485,9 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         if (g == cq.pend - 1 || g == g1 - 1) {
             finish_segment(g);
             if (g + 1 < g1) {
-                cq = next_req(p, dw, cq);
+                // (requests without pages hold no flat page: skip them)
+                do cq = next_req(p, dw, cq);
+                while (cq.pend == cq.pfx);
                 seg_g = g + 1;
                 load_q();
 #pragma unroll
@@ -525,7 +528,10 @@ template <int D, int HW>
 __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeWork dw) {
     constexpr int MB = D / 16;
     const int hg = blockIdx.x, i = blockIdx.y;
-    const int pfx = ld_meta(dw.dpfx, i), pend = ld_meta(dw.dpfx, i + 1);
+    const int r = dw.self_plan ? i : ld_meta(dw.dreq, i);
+    const int t0 = ld_meta(p.cu_q_lens, r);
+    if (dw.self_plan && ld_meta(p.cu_q_lens, r + 1) - t0 != 1) return;  // not a decode request
+    const int pfx = ld_meta(dw.dpfx, i), pend = pfx + blocks_of(ld_meta(p.context_lens, r));
     const int b_first = wg_of_page(pfx, dw.np, dw.nwg);
     const int b_last = wg_of_page(pend - 1, dw.np, dw.nwg);
     if (b_first == b_last) return;  // written by the decode kernel
@@ -534,8 +540,6 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
     const int G = p.Hq / p.Hkv;
     if (n16 >= G) return;
     const int hl = w * G + n16;  // q head inside the head group
-    const int r = ld_meta(dw.dreq, i);
-    const int t0 = ld_meta(p.cu_q_lens, r);
     // One pass with a running max; the slots are read kU at a time so that
     // their loads are in flight together (a request rarely spans more than
     // two or three workgroups).

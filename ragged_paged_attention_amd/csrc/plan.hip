@@ -68,10 +68,12 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     const size_t part_heads = std::max(slot_heads(pl.decode_hw), slot_heads(hw_long));
     const int cap_max = std::max(wg_cap(pl.decode_hw), wg_cap(hw_long));
     size_t off = 0;
+    // The decode list holds the decode requests (plan kernel) or every
+    // request (no plan kernel): R entries cover both.
     pl.off_dreq = off;
-    off = align256(off + sizeof(int32_t) * (size_t)nd);
+    off = align256(off + sizeof(int32_t) * (size_t)(nd ? R : 0));
     pl.off_dpfx = off;
-    off = align256(off + sizeof(int32_t) * ((size_t)nd + 1));
+    off = align256(off + sizeof(int32_t) * (size_t)(nd ? R + 1 : 0));
     pl.off_wstart = off;
     off = align256(off + sizeof(int32_t) * (size_t)(nd ? cap_max : 0));
     pl.off_part_o = off;
@@ -257,19 +259,19 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
     dw.hw = plan.decode_hw;
-    // Batches of one kind (every request one new token, or none with one new
-    // token) skip the plan kernel: the decode or prefill kernel finds its
-    // own work.
+    // Batches of at most kSelfPlanReqs requests skip the plan kernel: the
+    // decode and prefill kernels find their own work, and the decode list is
+    // then every request of the batch.
     const bool self_plan = p.R <= kSelfPlanReqs && env_int("RA_SELF_PLAN", 1) != 0;
-    dw.self_plan = (self_plan && plan.n_prefill_reqs == 0 && dw.nd == p.R) ? 1 : 0;
-    const bool prefill_self = self_plan && plan.n_decode_reqs == 0 && plan.n_prefill_items > 0;
+    const bool has_decode = plan.n_decode_reqs > 0, has_prefill = plan.n_prefill_items > 0;
+    dw.self_plan = self_plan ? 1 : 0;
+    if (self_plan && has_decode) dw.nd = p.R;
     hipError_t err = hipSuccess;
     // A batch with both kinds of work runs its prefill kernel beside the
     // decode kernel (not when the caller times the stages), and the decode
-    // kernel then leaves a quarter of the compute units to it at first.
-    const bool overlap = !ev.events && dw.nd > 0 && plan.n_prefill_items > 0 &&
-                         env_int("RA_MIXED_OVERLAP", 1) != 0;
-    if (dw.nd > 0) {
+    // kernel then leaves part of the compute units to it at first.
+    const bool overlap = !ev.events && has_decode && has_prefill && env_int("RA_MIXED_OVERLAP", 1) != 0;
+    if (has_decode) {
         err = decode_workgroups(p, plan, &dw.nwg);
         if (err != hipSuccess) return err;
         if (overlap) {
@@ -289,7 +291,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    if (!dw.self_plan && !prefill_self) {
+    if (!self_plan) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
                            p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg,
                            (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
@@ -306,16 +308,16 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         if (err == hipSuccess) err = hipEventRecord(ss->fork, stream);
         if (err == hipSuccess) err = launch_decode(p, dw, stream, ev);
         if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
-        if (err == hipSuccess) err = launch_prefill(p, plan, pre, false, ss->s);
+        if (err == hipSuccess) err = launch_prefill(p, plan, pre, self_plan, ss->s);
         if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
         if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
         return err;
     }
     err = ev.record(1);
-    if (err == hipSuccess && plan.n_prefill_items > 0) err = launch_prefill(p, plan, pre, prefill_self, stream);
+    if (err == hipSuccess && has_prefill) err = launch_prefill(p, plan, pre, self_plan, stream);
     if (err == hipSuccess) err = ev.record(2);
     if (err == hipSuccess) {
-        if (dw.nd > 0) {
+        if (has_decode) {
             err = launch_decode(p, dw, stream, ev);  // records event 3 between its kernels
         } else {
             err = ev.record(3);

@@ -14,10 +14,12 @@
 //
 // Prefill: chunks are cut into query tiles of `q_tile` tokens per kv head.
 //
-// The host computes counts and the workspace layout only; a one-workgroup
-// plan kernel writes the decode request lists, the workgroup start table and
-// the prefill items from the device copies of the same metadata, so no
-// host-to-device copy is needed.
+// The host computes counts and the workspace layout only.  Batches of at
+// most kSelfPlanReqs requests need no further planning: the decode and
+// prefill kernels find their own work from the device metadata.  Larger
+// batches run a one-workgroup plan kernel that writes the decode request
+// list, the workgroup start table and the prefill items from the device
+// copies of the same metadata, so no host-to-device copy is needed.
 #pragma once
 
 #include <stddef.h>
@@ -30,13 +32,12 @@
 
 namespace ra {
 
-// Largest batch whose decode kernel (decode requests only) or prefill kernel
-// (no decode requests) finds its own work with a wave scan over the
-// requests; larger and mixed batches run the plan kernel.
+// Largest batch whose decode and prefill kernels find their own work with a
+// wave scan over the requests; larger batches run the plan kernel.
 constexpr int kSelfPlanReqs = 512;
 
-// Prefill item k of a batch without decode requests (at most kSelfPlanReqs
-// requests), found without the plan kernel: the item the plan kernel would
+// Prefill item k of a batch of at most kSelfPlanReqs requests, found
+// without the plan kernel: the item the plan kernel would
 // write at position k (requests in order; per request its query tiles,
 // longest key range first, each for every kv head).  Every lane of the
 // calling wavefront must take part: lane l holds requests l, l + 64, ...
@@ -110,15 +111,15 @@ struct Plan {
 // The decode work description the decode kernel reads (all in the workspace).
 struct DecodeWork {
     const int32_t *dreq;    // [nd]      request id of the i-th decode request
-    const int32_t *dpfx;    // [nd + 1]  first flat page of decode request i
+    const int32_t *dpfx;    // [nd]      first flat page of decode request i
     const int32_t *wstart;  // [nwg]     decode request holding workgroup b's first page
     float *part_o;          // [nhg][nwg][2][HW*G][D] partial o (unnormalised)
     float *part_ml;         // [nhg][nwg][2][HW*G][2] partial (m, l)
     int nd, np, nwg;        // decode requests, flat pages, workgroups per head group
     int hw;                 // kv heads per workgroup
-    int self_plan;          // 1: every request is a decode request, dreq is the identity and
-                            // the decode kernel finds its own start (no plan kernel); it then
-                            // writes dreq / dpfx for the merge kernel
+    int self_plan;          // 1: no plan kernel; the list is every request of the batch (nd =
+                            // R, dreq unused), the decode kernel finds its own start and writes
+                            // dpfx of the decode requests for the merge kernel
 };
 
 // Optional hipEvents recorded at the stage boundaries of one call.

@@ -181,12 +181,16 @@ def test_decode_with_few_workgroups(wgs, monkeypatch):
     check_small(b, "specialised")
 
 
-def test_self_planned_decode_matches_plan_kernel(monkeypatch):
-    """A decode-only batch finds its work split inside the decode kernel; with
-    the plan kernel forced instead (RA_SELF_PLAN=0) the split, and so every
-    output bit, is the same."""
+@pytest.mark.parametrize("mixed", [False, True])
+def test_self_planned_decode_matches_plan_kernel(mixed, monkeypatch):
+    """A batch of at most 512 requests finds its decode work split (and its
+    prefill items) inside the kernels; with the plan kernel forced instead
+    (RA_SELF_PLAN=0) the split, and so every output bit, is the same."""
     ctx = [5000, 3, 1700, 16, 31, 4096, 900, 0, 2500, 7000, 64]
-    b = build_batch([1] * len(ctx), ctx, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=78,
+    q = [1] * len(ctx)
+    if mixed:  # prefill chunks and empty requests between the decode requests
+        q[1], q[4], q[7], q[9] = 40, 0, 130, 0
+    b = build_batch(q, ctx, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=78,
                     name="self_plan")
     out_self, kc_self, _ = run_gpu(b)
     monkeypatch.setenv("RA_SELF_PLAN", "0")
