@@ -200,6 +200,38 @@ __device__ __forceinline__ int2 self_plan_first(const Params &p, const DecodeWor
     return make_int2(__builtin_amdgcn_readfirstlane(first), __builtin_amdgcn_readfirstlane(first_pfx));
 }
 
+// Whole-request ranges (short contexts, no plan kernel): workgroup b takes
+// list entries [x0, x1); returns the flat pages {before x0, before x1}, from
+// the same wave scan as above.
+__device__ __forceinline__ int2 self_plan_range(const Params &p, int x0, int x1) {
+    constexpr int KR = kSelfPlanReqs / 64;
+    const int lane = threadIdx.x & 63, R = p.R;
+    int nb[KR];
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        const int r = 64 * k + lane;
+        const bool decode = r < R && p.cu_q_lens[r + 1] - p.cu_q_lens[r] == 1;
+        nb[k] = decode ? blocks_of(p.context_lens[r]) : 0;
+    }
+    int base = 0, at0 = 0, at1 = 0;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        if (64 * k >= R) break;
+        int incl = nb[k];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
+        }
+        const int excl = base + incl - nb[k];
+        if (x0 >= 64 * k && x0 < 64 * k + 64) at0 = __shfl(excl, x0 - 64 * k, 64);
+        if (x1 >= 64 * k && x1 < 64 * k + 64) at1 = __shfl(excl, x1 - 64 * k, 64);
+        base += __shfl(incl, 63, 64);
+    }
+    if (x1 >= R) at1 = base;
+    return make_int2(__builtin_amdgcn_readfirstlane(at0), __builtin_amdgcn_readfirstlane(at1));
+}
+
 // Workgroup holding flat page g when NP pages are cut into nwg equal ranges
 // [floor(b NP / nwg), floor((b+1) NP / nwg)).
 __device__ __forceinline__ int wg_of_page(long long g, int np, int nwg) {
@@ -226,8 +258,18 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     const int n16 = lane & 15, kg = lane >> 4;
     const int hg = blockIdx.x, b = blockIdx.y;
     const int np = dw.np, nwg = dw.nwg;
-    const int g0 = (int)(((long long)b * np) / nwg);
-    const int g1 = (int)(((long long)(b + 1) * np) / nwg);
+    // The workgroup's flat pages [g0, g1): an equal share of all pages, or
+    // (whole-request mode) the pages of an equal share of the requests.
+    int g0, g1, x0 = 0;
+    if (dw.whole) {
+        x0 = (int)(((long long)b * dw.nd) / nwg);
+        const int2 g = self_plan_range(p, x0, (int)(((long long)(b + 1) * dw.nd) / nwg));
+        g0 = g.x;
+        g1 = g.y;
+    } else {
+        g0 = (int)(((long long)b * np) / nwg);
+        g1 = (int)(((long long)(b + 1) * np) / nwg);
+    }
     if (g0 >= g1) return;
     const int Hkv = p.Hkv, G = p.Hq / Hkv;
     const int hk0 = hg * HW;   // first kv head of this workgroup
@@ -257,7 +299,9 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     // belong to), so that the page loop never waits on a memory round trip
     // for an id --------------------------------------------------------------
     DecodeReq first_q;
-    if (dw.self_plan) {
+    if (dw.whole) {
+        first_q = make_req(p, dw, x0, g0);
+    } else if (dw.self_plan) {
         const int2 f = self_plan_first(p, dw, g0, g1, hg == 0 && w == 0);
         first_q = make_req(p, dw, f.x, f.y);
     } else {
@@ -335,6 +379,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
 
     // ---- compute cursor: the request being accumulated ---------------------
     DecodeReq cq = lq;
+    while (cq.pend == cq.pfx) cq = next_req(p, dw, cq);  // (a range may start at a request without pages)
     int seg_g = g0;  // first flat page of the current segment
     short8_t qb[KS];
     // Q^T as the B operand: lane (head n16, group kg) holds q[t0][hk*G + n16][32ks + 8kg .. +8].
@@ -428,8 +473,9 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     auto finish_segment = [&](int g_last) {
         float l_tot = l_run + __shfl_xor(l_run, 16, 64);
         l_tot += __shfl_xor(l_tot, 32, 64);
-        const int b_first = wg_of_page(cq.pfx, np, nwg);
-        const int b_last = wg_of_page(cq.pend - 1, np, nwg);
+        // (whole-request ranges never cut a request)
+        const int b_first = dw.whole ? b : wg_of_page(cq.pfx, np, nwg);
+        const int b_last = dw.whole ? b : wg_of_page(cq.pend - 1, np, nwg);
         const bool hv = n16 < G;
         const int h = hk * G + n16;  // q head
         bf16_t *orow = p.out + ((size_t)cq.t0 * p.Hq + h) * D;
@@ -624,6 +670,7 @@ hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t 
     if (e != hipSuccess) return e;
     e = ev.record(3);
     if (e != hipSuccess) return e;
+    if (dw.whole) return hipSuccess;  // no request is cut: nothing to merge
     const dim3 mgrid(p.Hkv / HW, dw.nd);
     hipLaunchKernelGGL((decode_merge_kernel<D, HW>), mgrid, dim3(64 * HW), 0, stream, p, dw);
     return hipGetLastError();
@@ -681,7 +728,7 @@ int decode_heads_per_group(int D, int Hkv, long long blocks, int nd) {
     return 1;
 }
 
-hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg) {
+hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *nwg) {
     int cap = 0;
     hipError_t e;
     switch (p.D) {
@@ -699,7 +746,7 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg) {
     if (forced > 0) cap = forced * plan.decode_hgroups;
     int n = std::max(1, cap / plan.decode_hgroups);
     n = std::min(n, plan.decode_wg_cap);
-    n = std::min(n, std::max(1, plan.n_decode_pages / kMinPages));
+    n = std::min(n, whole > 0 ? whole : std::max(1, plan.n_decode_pages / kMinPages));
     *nwg = n;
     return hipSuccess;
 }

@@ -27,7 +27,9 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
         const int q = cu[r + 1] - cu[r];
         if (q == 1) {
             ++pl.n_decode_reqs;
-            np += ceil_div((long long)ctx[r] + 1, 16);  // 16-row blocks of pages
+            const long long nb = ceil_div((long long)ctx[r] + 1, 16);  // 16-row blocks of pages
+            np += nb;
+            pl.max_decode_pages = (int)std::max<long long>(pl.max_decode_pages, nb);
         } else if (q > 1) {
             ++pl.n_prefill_reqs;
         }
@@ -266,13 +268,21 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     const bool has_decode = plan.n_decode_reqs > 0, has_prefill = plan.n_prefill_items > 0;
     dw.self_plan = self_plan ? 1 : 0;
     if (self_plan && has_decode) dw.nd = p.R;
+    // Short contexts (at most 40 16-row blocks per decode request on
+    // average, none longer than four times the mean): whole requests per
+    // workgroup, an equal share of the list each, so no request is cut and
+    // no merge kernel runs.
+    const long long nd_dec = plan.n_decode_reqs, np_dec = plan.n_decode_pages;
+    dw.whole = (self_plan && has_decode && np_dec <= 40 * nd_dec &&
+                (long long)plan.max_decode_pages * nd_dec <= 4 * np_dec &&
+                env_int("RA_DECODE_WHOLE", 1) != 0) ? 1 : 0;
     hipError_t err = hipSuccess;
     // A batch with both kinds of work runs its prefill kernel beside the
     // decode kernel (not when the caller times the stages), and the decode
     // kernel then leaves part of the compute units to it at first.
     const bool overlap = !ev.events && has_decode && has_prefill && env_int("RA_MIXED_OVERLAP", 1) != 0;
     if (has_decode) {
-        err = decode_workgroups(p, plan, &dw.nwg);
+        err = decode_workgroups(p, plan, dw.whole ? dw.nd : 0, &dw.nwg);
         if (err != hipSuccess) return err;
         if (overlap) {
             const int per_mille = env_int("RA_MIXED_DECODE_SHARE", plan.decode_share_pm);

@@ -92,6 +92,7 @@ struct Plan {
     int n_decode_reqs = 0, n_prefill_reqs = 0;
     // decode
     int n_decode_pages = 0;     // NP: pages of all decode requests
+    int max_decode_pages = 0;   // pages of the longest decode request
     int decode_hw = 0;          // kv heads per decode workgroup
     int decode_hgroups = 0;     // Hkv / decode_hw
     int decode_wg_cap = 0;      // workgroups per head group the workspace is sized for
@@ -117,6 +118,8 @@ struct DecodeWork {
     float *part_ml;         // [nhg][nwg][2][HW*G][2] partial (m, l)
     int nd, np, nwg;        // decode requests, flat pages, workgroups per head group
     int hw;                 // kv heads per workgroup
+    int whole;              // 1: workgroup b takes the whole requests [b nd / nwg, (b+1) nd / nwg)
+                            // of the list (short contexts, self_plan only): nothing to merge
     int self_plan;          // 1: no plan kernel; the list is every request of the batch (nd =
                             // R, dreq unused), the decode kernel finds its own start and writes
                             // dpfx of the decode requests for the merge kernel
@@ -142,8 +145,9 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
 // kv heads per decode workgroup for this head_dim, kv-head count and batch
 // (blocks: 16-row page blocks of all nd decode requests).
 int decode_heads_per_group(int D, int Hkv, long long blocks, int nd);
-// Decode workgroups per head group to launch on the current device.
-hipError_t decode_workgroups(const Params &p, const Plan &plan, int *nwg);
+// Decode workgroups per head group to launch on the current device (whole:
+// list entries when each workgroup takes whole requests, else 0).
+hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *nwg);
 // Launches the decode kernel, records event 3, launches the merge kernel.
 hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream,
                          const StageEvents &ev);

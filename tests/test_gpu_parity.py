@@ -150,6 +150,10 @@ EDGES = {
     "decode_only_512": ([1] * 512, [(29 * i) % 300 for i in range(512)], 8, 2, 64),
     "decode_only_513": ([1] * 513, [(29 * i) % 300 for i in range(513)], 8, 2, 64),
     "decode_and_empty": ([1, 0, 1, 1, 0, 1], [3000, 50, 2000, 16, 7, 1200], 32, 8, 128),
+    # short contexts: whole requests per decode workgroup (no merge), also
+    # with prefill chunks and empty requests in the batch
+    "short_whole_requests": ([1] * 70, [(17 * i) % 90 for i in range(70)], 32, 8, 128),
+    "short_whole_mixed": ([1, 1, 5, 1, 0, 1, 1, 33, 1, 1] * 6, [(23 * i) % 70 for i in range(60)], 16, 8, 256),
     # prefill-only batches likewise find their items in the prefill kernel
     "prefill_only_512": ([2 + (i % 5) for i in range(512)], [(13 * i) % 40 for i in range(512)], 8, 2, 64),
     "prefill_only_513": ([2 + (i % 5) for i in range(513)], [(13 * i) % 40 for i in range(513)], 8, 2, 64),
