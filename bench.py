@@ -104,9 +104,13 @@ def prefill_requests(b: Batch):
 # were taken on.
 # ---------------------------------------------------------------------------
 def kernel_source_hash(stage: str) -> str:
-    name = {"decode": "decode.hip", "prefill": "prefill.hip"}[stage]
-    data = open(os.path.join(ROOT, "ragged_paged_attention_amd", "csrc", name), "rb").read()
-    return hashlib.sha256(data).hexdigest()[:16]
+    """Hash of the sources the stage's kernel is compiled from (its file and
+    the device headers it includes)."""
+    names = ({"decode": "decode.hip", "prefill": "prefill.hip"}[stage], "common.hpp", "plan.hpp")
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "ragged_paged_attention_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(stage: str, workload: str):
