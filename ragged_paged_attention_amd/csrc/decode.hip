@@ -573,7 +573,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
 template <int D, int HW>
 __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeWork dw) {
     constexpr int MB = D / 16;
-    const int hg = blockIdx.x, i = blockIdx.y;
+    const int i = blockIdx.x, hg = blockIdx.y;  // (requests on x: more than 65535 of them fit)
     const int r = dw.self_plan ? i : ld_meta(dw.dreq, i);
     const int t0 = ld_meta(p.cu_q_lens, r);
     if (dw.self_plan && ld_meta(p.cu_q_lens, r + 1) - t0 != 1) return;  // not a decode request
@@ -671,7 +671,7 @@ hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t 
     e = ev.record(3);
     if (e != hipSuccess) return e;
     if (dw.whole) return hipSuccess;  // no request is cut: nothing to merge
-    const dim3 mgrid(p.Hkv / HW, dw.nd);
+    const dim3 mgrid(dw.nd, p.Hkv / HW);
     hipLaunchKernelGGL((decode_merge_kernel<D, HW>), mgrid, dim3(64 * HW), 0, stream, p, dw);
     return hipGetLastError();
 }

@@ -222,6 +222,16 @@ def test_self_planned_prefill_matches_plan_kernel(D, monkeypatch):
     assert_close(out_self, ref, "self_plan_pre")
 
 
+def test_more_decode_requests_than_a_grid_dimension():
+    """70000 decode requests (more than 65535: the merge kernel's grid puts
+    requests on its x dimension) with short contexts, through the plan kernel;
+    the requests cut at workgroup boundaries go through the merge kernel."""
+    n = 70000
+    b = build_batch([1] * n, [(7 * i) % 40 for i in range(n)], num_q_heads=4, num_kv_heads=1, head_dim=64,
+                    seed=80, name="decode_70000")
+    check_small(b, "specialised")
+
+
 def test_fresh_decode_returns_v_new():
     b = build_batch([1, 1], [0, 0], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=3)
     out, _, _ = run_gpu(b)
