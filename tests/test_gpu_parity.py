@@ -115,6 +115,8 @@ PAGED = [
     (34, 64, 4, 40, 500, 16, 8, 256, 0.5, True),
     (35, 128, 4, 90, 700, 8, 8, 128, 0.4, False),
     (36, 32, 8, 1, 2000, 32, 8, 128, 1.0, True),   # decode only, several splits
+    (37, 1024, 5, 60, 3000, 16, 4, 128, 0.5, True),  # the largest page size
+    (38, 1024, 6, 1, 5000, 8, 8, 64, 1.0, True),     # largest page size, decode only
 ]
 
 
@@ -229,6 +231,14 @@ def test_more_decode_requests_than_a_grid_dimension():
     n = 70000
     b = build_batch([1] * n, [(7 * i) % 40 for i in range(n)], num_q_heads=4, num_kv_heads=1, head_dim=64,
                     seed=80, name="decode_70000")
+    check_small(b, "specialised")
+
+
+def test_very_long_contexts():
+    """A decode request at 131072 tokens of context and an 8-token chunk after
+    65536, next to short requests (Llama-3-8B head shapes)."""
+    b = build_batch([1, 8, 1, 3], [131072, 65536, 5, 70], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                    seed=81, name="very_long")
     check_small(b, "specialised")
 
 
