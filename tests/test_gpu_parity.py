@@ -242,6 +242,57 @@ def test_very_long_contexts():
     check_small(b, "specialised")
 
 
+@pytest.mark.parametrize("n_decode", [40, 600])
+def test_graph_capture_replays_match_eager(n_decode):
+    """The call captured in a HIP graph (torch.cuda.graph) and replayed three
+    times, with eager calls in between, gives the eager call's bits every
+    time, and reads inputs changed in place.  40 decode requests plus
+    prefill chunks plan inside the kernels and fork the prefill kernel onto
+    the side stream; 600 run the plan kernel first."""
+    q_lens = [1] * n_decode + [37, 130, 2]
+    ctx = [(53 * i) % 3000 for i in range(n_decode)] + [0, 700, 90]
+    b = build_batch(q_lens, ctx, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=82 + n_decode,
+                    name=f"graph_{n_decode}")
+    dev = torch.device("cuda:0")
+    q = b.q.to(dev)
+    t = [x.to(dev) for x in (b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table, b.cu_q_lens,
+                             b.context_lens, b.slot_mapping)]
+
+    def call(q_in):
+        return binding.forward(q_in, *t, causal=b.causal, cu_q_lens_host=b.cu_q_lens,
+                               context_lens_host=b.context_lens)
+
+    want = call(q).clone()
+    q2 = torch.flip(q, dims=[0]).contiguous()
+    want2 = call(q2).clone()
+    kc_want = t[2].clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream, as for any capture
+        call(q)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    q_static = q.clone()
+    with torch.cuda.graph(g):
+        out = call(q_static)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(t[2].view(torch.int16), kc_want.view(torch.int16)), f"replay {rep}: cache"
+        eager = call(q2)  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(eager.view(torch.int16), want2.view(torch.int16))
+    q_static.copy_(q2)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), want2.view(torch.int16)), "replay after changing q"
+    ref, _, _ = oracle_full(b)
+    assert_close(want.cpu(), ref, f"graph_{n_decode}")
+
+
 def test_fresh_decode_returns_v_new():
     b = build_batch([1, 1], [0, 0], num_q_heads=8, num_kv_heads=2, head_dim=128, seed=3)
     out, _, _ = run_gpu(b)
