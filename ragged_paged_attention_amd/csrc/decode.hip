@@ -7,7 +7,12 @@
 // walks its range request by request ("segments"); a segment that is a whole
 // request writes the output, otherwise the workgroup writes a partial
 // (m, l, o) to a slot of its own, and a small merge kernel that follows
-// combines the partials of each such request by log-sum-exp.
+// combines the partials of each such request by log-sum-exp.  Batches of
+// short contexts instead give each workgroup whole requests (an equal share
+// of the request list), so nothing is cut and no merge kernel runs.  Up to
+// kSelfPlanReqs requests the workgroups find their ranges themselves (a wave
+// scan over the requests' page counts); larger batches read the start table
+// the plan kernel writes.
 //
 // One wavefront per kv head; the G = Hq/Hkv query heads of a kv head share
 // every K/V byte its wavefront reads (grouped-query attention), so the cache

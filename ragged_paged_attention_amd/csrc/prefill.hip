@@ -4,7 +4,9 @@
 // 256 runs prefill_kernel, described here.
 //
 // Work unit: one workgroup of NW wavefronts per (request r, kv head hk, query
-// tile of ROWS/G tokens).  Its ROWS query rows are the G query heads of the
+// tile of ROWS/G tokens), read from the plan kernel's item list or, for
+// batches of at most kSelfPlanReqs requests, found by the workgroup itself
+// (self_plan_prefill_item).  Its ROWS query rows are the G query heads of the
 // group times the tile's tokens, so one K/V tile in LDS serves every head
 // that reads it (grouped-query attention).  Wavefront w owns MW consecutive
 // rows (two 32-row halves when MW = 64): each K or V element it reads from
