@@ -342,26 +342,29 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
         }
     };
     auto masked_tile = [&](int tile) { return tile * N + N - 1 > wave_lim_min; };
-    // P^T = exp2(S^T * scale - m) of half h as bf16 B operands, and row sums.
+    // P^T = exp2(S^T * scale - m) of half h as bf16 B operands; returns the
+    // lane's sum of those bf16 values (the row sum is taken over the same
+    // rounded P that the PV product uses, so the weights sum to one).
     auto pack = [&](const float (&pe)[NE], short8_t (&pb)[N / 16]) {
+        float lsum = 0.f;
 #pragma unroll
         for (int s16 = 0; s16 < N / 16; ++s16) {
             uint32_t w4[4];
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) w4[e2] = cvt_pk_bf16(pe[8 * s16 + 2 * e2], pe[8 * s16 + 2 * e2 + 1]);
+            for (int e2 = 0; e2 < 4; ++e2) {
+                w4[e2] = cvt_pk_bf16(pe[8 * s16 + 2 * e2], pe[8 * s16 + 2 * e2 + 1]);
+                lsum = pair_sum_bf16(w4[e2], lsum);
+            }
             pb[s16] = __builtin_bit_cast(short8_t, w4);
         }
+        return lsum;
     };
     auto tail = [&](int h, const float16_t (&s)[KB], short8_t (&pb)[N / 16]) {
         const float nref = -m_run[h];
-        float pe[NE], lsum = 0.f;
+        float pe[NE];
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-            pe[e] = fast_exp2(fmaf(s[e / 16][e % 16], sl2, nref));
-            lsum += pe[e];
-        }
-        l_run[h] += lsum;
-        pack(pe, pb);
+        for (int e = 0; e < NE; ++e) pe[e] = fast_exp2(fmaf(s[e / 16][e % 16], sl2, nref));
+        l_run[h] += pack(pe, pb);
     };
     // O^T += V^T . P^T over the tile in `stage`, 16 keys per MFMA; each V^T
     // read feeds every half.
@@ -401,11 +404,10 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
         const bf16_t *Ks = smem + ((t + 1) % NSTAGE) * 2 * TILE;
         const bf16_t *Vs = smem + (t % NSTAGE) * 2 * TILE + TILE;
         // ---- phase A
-        float nref[NH], lsum[NH], pe[NH][NE];
+        float nref[NH], pe[NH][NE];
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             nref[h] = -m_run[h];
-            lsum[h] = 0.f;
         }
         short8_t ka[2][KB];
 #pragma unroll
@@ -427,14 +429,12 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
             for (int x = 0; x < EA; ++x) {
                 const int f = ks * EA + x, h = f / NE, e = f % NE;
                 pe[h][e] = fast_exp2(fmaf(s_cur[h][e / 16][e % 16], sl2, nref[h]));
-                lsum[h] += pe[h][e];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-            l_run[h] += lsum[h];
-            pack(pe[h], pb[h]);
+            l_run[h] += pack(pe[h], pb[h]);
         }
         // ---- phase B
         int thr[NH];
@@ -815,8 +815,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
                 const int e = 8 * s16 + 2 * e2;
                 const float a = fast_exp2(fmaf(s[e / 16][e % 16], sl2, nref));
                 const float b = fast_exp2(fmaf(s[(e + 1) / 16][(e + 1) % 16], sl2, nref));
-                lsum += a + b;
                 w4[e2] = cvt_pk_bf16(a, b);
+                lsum = pair_sum_bf16(w4[e2], lsum);  // the row sum of the rounded P
             }
             pb[s16] = __builtin_bit_cast(short8_t, w4);
         }
@@ -877,8 +877,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
                 const int e = ks * EA + x;
                 const float a = fast_exp2(fmaf(so[e / 16][e % 16], sl2, nref));
                 const float b = fast_exp2(fmaf(so[(e + 1) / 16][(e + 1) % 16], sl2, nref));
-                lsum += a + b;
                 pk[e / 2] = cvt_pk_bf16(a, b);
+                lsum = pair_sum_bf16(pk[e / 2], lsum);  // the row sum of the rounded P
             }
             __builtin_amdgcn_sched_barrier(0);
         }

@@ -62,7 +62,10 @@ def assert_close(out: torch.Tensor, ref: np.ndarray, what=""):
     assert not np.isnan(o).any(), f"{what}: NaN in output"
     err = np.abs(o - ref)
     worst = float(err.max(initial=0.0))
-    assert worst <= TOL, f"{what}: max abs error {worst:.3g} > {TOL}"
+    if worst > TOL:
+        idx = np.unravel_index(int(np.argmax(err)), err.shape)
+        raise AssertionError(f"{what}: max abs error {worst:.3g} > {TOL} at (token, head, dim) {idx}: "
+                             f"GPU {o[idx]:.6g}, oracle {ref[idx]:.6g}")
     return worst
 
 
@@ -291,6 +294,16 @@ def test_graph_capture_replays_match_eager(n_decode):
     assert torch.equal(out.view(torch.int16), want2.view(torch.int16)), "replay after changing q"
     ref, _, _ = oracle_full(b)
     assert_close(want.cpu(), ref, f"graph_{n_decode}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("scale,D", [(0.3, 128), (0.02, 64), (0.125, 256)])
+def test_explicit_softmax_scale(scale, D, variant):
+    """A softmax scale other than 1/sqrt(D), on decode requests and prefill
+    chunks with context, both variants."""
+    b = build_batch([1, 70, 1, 33], [900, 150, 20, 0], num_q_heads=16, num_kv_heads=4, head_dim=D,
+                    scale=scale, seed=int(1000 * scale) + D, name=f"scale_{scale}_{D}")
+    check_small(b, variant)
 
 
 def test_fresh_decode_returns_v_new():
