@@ -137,6 +137,8 @@ def test_forward_rejects_before_touching_the_gpu(lib):
     cu, ctx = b.cu_q_lens.clone(), b.context_lens.clone()
     assert _forward_status(lib, shape_for(b, head_dim=96), cu, ctx) == 3  # unsupported
     assert _forward_status(lib, shape_for(b, page_size=24), cu, ctx) == 3  # not a multiple of 16
+    assert _forward_status(lib, shape_for(b, num_q_heads=64, num_kv_heads=2), cu, ctx) == 3  # G = 32 > 16
+    assert _forward_status(lib, shape_for(b, page_size=2048), cu, ctx) == 3  # page above 1024
     assert _forward_status(lib, shape_for(b, num_kv_heads=3), cu, ctx) == 2
     assert _forward_status(lib, shape_for(b), cu, ctx, ws_bytes=16) == 5  # workspace too small
     assert _forward_status(lib, shape_for(b), cu, ctx, ws_ptr=0x100010) == 5  # misaligned
