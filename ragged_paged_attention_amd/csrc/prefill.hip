@@ -108,6 +108,10 @@ constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 
 #ifndef RA_PREFILL_PINGPONG
 #define RA_PREFILL_PINGPONG 1
 #endif
+// 1: head_dim 256 uses it too.
+#ifndef RA_PREFILL_PP256
+#define RA_PREFILL_PP256 1
+#endif
 
 template <int D>
 struct PrefillShape;
@@ -572,21 +576,30 @@ using ic = std::integral_constant<int, I>;
 
 template <int D>
 struct PingPongCfg {
-    static constexpr int NW = 8, MW = 32, N = 64;
+    // 64-key tiles up to head_dim 128; 32-key tiles at 256 (the same 32 MFMAs
+    // per tile and wavefront, and four stages still fit in LDS).
+    static constexpr int NW = 8, MW = 32, N = D > 128 ? 32 : 64;
     static constexpr int NTHR = 64 * NW, ROWS = NW * MW;
     static constexpr int KB = N / 32, KS = D / 16, MD = D / 32, CPR = D / 8;
     static constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // K chunk swizzle mask
     static constexpr int VSS = CPR >= 16 ? 4 : 2;           // V chunk swizzle step
     static constexpr int TILE = N * D;                      // elements of one K (or V) tile
+    static constexpr int RWL = N / 4;                       // key rows per loading wave and tile
     static constexpr int RPI = 64 / CPR;                    // rows per 1 KiB wavefront load
-    static constexpr int IPL = 16 / RPI;                    // loads per loading wave, tensor and tile
+    static constexpr int IPL = RWL / RPI;                   // loads per loading wave, tensor and tile
     static constexpr int NE = KB * 16;                      // scores per lane and tile
-    static constexpr int EA = NE / KS;                      // exponentials per A chunk
+    static constexpr int EP = NE / 2;                       // exponential pairs per lane and tile
     static constexpr int NB = (N / 16) * MD;                // B chunks
     static constexpr int EB = NE / NB;                      // row-max elements per B chunk
     static constexpr int KPF = RA_PP_KPF, VPF = RA_PP_VPF;  // LDS read prefetch depth (k-steps, B chunks)
-    static_assert(N == 64, "group 0's four waves load one 16-row page each");
-    static_assert(EA % 2 == 0 && EB >= 1 && NE % KS == 0 && NE % NB == 0, "chunks split the scores evenly");
+    // The last QKS k-steps of Q^T sit in LDS instead of registers at head_dim
+    // 256, where O (128 registers) and all of Q^T (64) would leave too few
+    // registers for two wavefronts per SIMD; 32 KiB, so LDS holds 160 KiB.
+    static constexpr int QKS = D > 128 ? 4 : 0;
+    static constexpr int KQR = KS - QKS;                    // k-steps of Q^T in registers
+    static constexpr int QCH = 2 * QKS;                     // 16-byte chunks per row in LDS
+    static_assert(16 % RWL == 0 && RWL % RPI == 0, "a loading wave's rows of a tile lie in one 16-row block");
+    static_assert(EB >= 1 && NE % NB == 0, "B chunks split the scores evenly");
 };
 
 template <int D>
@@ -594,12 +607,16 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
                                                             int q_tile) {
     using C = PingPongCfg<D>;
     constexpr int ROWS = C::ROWS, N = C::N, KB = C::KB, KS = C::KS, MD = C::MD, CPR = C::CPR,
-                  SWM = C::SWM, VSS = C::VSS, TILE = C::TILE, RPI = C::RPI, IPL = C::IPL,
-                  NTHR = C::NTHR, NE = C::NE, EA = C::EA, NB = C::NB, EB = C::EB, KPF = C::KPF,
-                  VPF = C::VPF;
+                  SWM = C::SWM, VSS = C::VSS, TILE = C::TILE, RWL = C::RWL, RPI = C::RPI, IPL = C::IPL,
+                  NTHR = C::NTHR, NE = C::NE, EP = C::EP, NB = C::NB, EB = C::EB, KPF = C::KPF,
+                  VPF = C::VPF, KQR = C::KQR, QCH = C::QCH;
     // One array per stage and tensor (see above).
     __shared__ __attribute__((aligned(16))) bf16_t k0[TILE], k1[TILE], k2[TILE], k3[TILE];
     __shared__ __attribute__((aligned(16))) bf16_t v0[TILE], v1[TILE], v2[TILE], v3[TILE];
+    // Q^T k-steps KQR .. KS-1: row R's chunk c at c ^ ((R >> 1) & (QCH - 1)),
+    // so the 16 rows a 16-lane group reads hit 16 different bank groups.
+    // Every lane reads back only what it wrote itself.
+    __shared__ __attribute__((aligned(16))) bf16_t qlds[QCH ? ROWS * 8 * QCH : 8];
     auto kst = [&](auto s) -> bf16_t * {
         constexpr int S = decltype(s)::value;
         if constexpr (S == 0) return k0;
@@ -659,6 +676,13 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
         }
     }
 
+    // A value the compiler must recompute from here at each use instead of
+    // keeping derived values live across the loop, where registers are short.
+    auto opaque = [](uint32_t x) {
+        asm volatile("" : "+v"(x));
+        return x;
+    };
+
     // This lane's query row R = 32 w + n32: head g = R / QT, token i = R % QT.
     const int R = 32 * w + n32;
     const int gh = R / QT;
@@ -667,6 +691,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
     const int qi = q0 + (rvalid ? iq : 0);
     const int lim = rvalid ? (p.causal ? c + qi : L - 1) : -1;  // last visible key
     short8_t qb[KS];
+    const int qoff0 = QCH ? R * 8 * QCH + 8 * (h2 ^ ((R >> 1) & (QCH - 1))) : 0;
+    auto qoff = [&](int ks) { return (int)opaque((uint32_t)qoff0) ^ (16 * (ks - KQR)); };
     {
         // Q^T as the B operand: lane holds q[t0 + qi][hk*G + g][16ks + 8h2 .. +8].
         const bf16_t *qrow = p.q + ((size_t)(t0 + qi) * Hq + hk * G + gh) * D + 8 * h2;
@@ -674,49 +700,48 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const short8_t x = *reinterpret_cast<const short8_t *>(qrow + 16 * ks);
-            qb[ks] = rvalid ? x : z;
+            if (ks < KQR) qb[ks] = rvalid ? x : z;
+            else *reinterpret_cast<short8_t *>(qlds + qoff(ks)) = rvalid ? x : z;
         }
     }
+    auto q_lds = [&](int ks) { return *reinterpret_cast<const short8_t *>(qlds + qoff(ks)); };
     const int lim4 = lim - 4 * h2;             // masks compare key offsets inside a lane's group of 4
     const int wave_end = wave_max_i(lim + 1);  // keys this wavefront needs
     const int wave_lim_min = wave_min_i(rvalid ? lim : 0x7fffffff);
     const int ntw = min(ntiles, (wave_end + N - 1) / N);  // tiles this wavefront computes
 
-    // Loads (group 0 only): wavefront w fills key rows 16 w .. 16 w + 15 of a
-    // tile, one page of the cache or 16 rows of k_new / v_new.  Per-lane
+    // Loads (group 0 only): wavefront w fills key rows RWL w .. RWL w + RWL - 1
+    // of a tile, inside one 16-row block of a cache page or of k_new / v_new.  Per-lane
     // element offsets inside that row block (the chunk each lane fetches makes
     // the LDS layout swizzled: K chunk c of row j at c ^ (j & SWM), V chunk c
     // at c ^ VSS (j & 3)).
     auto v_swizzle = [](int row) { return ((row & 3) * VSS) & SWM; };
-    // Load u of a wavefront covers rows RPI u + lrow; since RPI u and lrow
-    // occupy disjoint bits, the K swizzle of load u is that of load 0 XOR a
-    // constant and the V swizzle does not depend on u: one base offset per
-    // tensor (bytes) plus a uniform row step.
+    // Load u of wavefront w covers tile rows RWL w + RPI u + lrow; the three
+    // terms occupy disjoint bits, so the swizzle of load u is that of lrow
+    // XOR a wave-uniform constant: one base offset per tensor (bytes) plus a
+    // uniform row step.
     const int lrow = l / CPR, lpc = l - lrow * CPR;
     const uint32_t lbase_k = 2u * ((lrow * Hkv + hk) * D + 8 * (lpc ^ (lrow & SWM)));
     const uint32_t lbase_v = 2u * ((lrow * Hkv + hk) * D + 8 * (lpc ^ v_swizzle(lrow)));
-    // The load addresses are recomputed at every issue (a few VALU of group 0)
-    // instead of being kept live across the loop, where registers are short.
-    auto opaque = [](uint32_t x) {
-        asm volatile("" : "+v"(x));
-        return x;
-    };
+    // (The load addresses are recomputed at every issue, through opaque, by a
+    // few VALU of group 0.)
     const size_t rstride = (size_t)Hkv * D;  // elements per token row
     const size_t ustride = 2 * RPI * rstride;  // bytes between loads u and u+1
     const bf16_t *const kcache = p.k_cache, *const vcache = p.v_cache;
     const bf16_t *const knew = p.k_new + (size_t)t0 * rstride, *const vnew = p.v_new + (size_t)t0 * rstride;
     auto issue_tile = [&](int tile, auto s) {
-        bf16_t *kd = kst(s) + 16 * w * D, *vd = vst(s) + 16 * w * D;
+        bf16_t *kd = kst(s) + RWL * w * D, *vd = vst(s) + RWL * w * D;
         const uint32_t bk = opaque(lbase_k), bv = opaque(lbase_v);
-        auto lofs_k = [&](int u) { return bk ^ (16u * ((RPI * u) & SWM)); };
-        const int jw = tile * N + 16 * w;  // first key row of this wavefront
-        if (jw + 15 < kv_end && (jw + 15 < c || jw >= c)) {
-            // The whole page is visible and comes from one tensor: uniform
+        auto lofs_k = [&](int u) { return bk ^ (16u * ((RWL * w + RPI * u) & SWM)); };
+        auto lofs_v = [&](int u) { return bv ^ (16u * (uint32_t)v_swizzle(RWL * w + RPI * u)); };
+        const int jw = tile * N + RWL * w;  // first key row of this wavefront
+        if (jw + RWL - 1 < kv_end && (jw + RWL - 1 < c || jw >= c)) {
+            // All RWL rows are visible and come from one tensor: uniform
             // base + 32-bit lane offset.
             const char *kb, *vb;
             if (jw < c) {
                 const size_t page = (size_t)ld_meta(p.page_table, prow + jw / p.S);
-                const size_t row0 = page * p.S + jw % p.S;  // 16 | S: the 16 rows share a page
+                const size_t row0 = page * p.S + jw % p.S;  // 16 | S: the RWL rows share a page
                 kb = (const char *)(kcache + row0 * rstride);
                 vb = (const char *)(vcache + row0 * rstride);
             } else {
@@ -726,10 +751,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 #pragma unroll
             for (int u = 0; u < IPL; ++u) {
                 load_lds16((const bf16_t *)(kb + u * ustride + lofs_k(u)), kd + RPI * u * D);
-                load_lds16((const bf16_t *)(vb + u * ustride + bv), vd + RPI * u * D);
+                load_lds16((const bf16_t *)(vb + u * ustride + lofs_v(u)), vd + RPI * u * D);
             }
         } else {
-            // The page holds the cache / new-token boundary or the last
+            // The rows hold the cache / new-token boundary or the last
             // visible key: per-lane sources; rows past the end repeat the
             // last visible key (finite, and masked).
             const int jp = min(jw, kv_end - 1);
@@ -739,7 +764,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
                 const int lr = (int)opaque(lrow);
                 const int kr = RPI * u + lr;
                 const int j = min(jw + kr, kv_end - 1);
-                const uint32_t d_k = lofs_k(u) - 2u * lr * Hkv * D, d_v = bv - 2u * lr * Hkv * D;
+                const uint32_t d_k = lofs_k(u) - 2u * lr * Hkv * D, d_v = lofs_v(u) - 2u * lr * Hkv * D;
                 const size_t crow = (page * p.S + j % p.S) * rstride;
                 const size_t nrow = (size_t)(j - c) * rstride;
                 const bool cached = j < c;
@@ -763,8 +788,16 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
         const int col = 16 * (n32 >> 4) + 4 * (l & 3);
         return vr0 * D + 8 * ((col >> 3) ^ v_swizzle(vr0)) + (col & 7);
     }();
-    auto koff = [&](int ks) { return koff0 ^ (16 * ks); };
-    auto voff = [&](int md) { return voff0 ^ (32 * md); };
+    // At head_dim 256 the XORs are redone at every read (one VALU each):
+    // kept live across the loop, the 24 offsets would push Q out of registers.
+    auto koff = [&](int ks) {
+        if constexpr (D > 128) return (int)opaque((uint32_t)koff0) ^ (16 * ks);
+        else return koff0 ^ (16 * ks);
+    };
+    auto voff = [&](int md) {
+        if constexpr (D > 128) return (int)opaque((uint32_t)voff0) ^ (32 * md);
+        else return voff0 ^ (32 * md);
+    };
     const float16_t zero16 = {};
     const float sl2 = p.scale_log2;
 
@@ -800,7 +833,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const short8_t a = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff(ks));
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[ks], ks ? s[kb] : zero16, 0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ks < KQR ? qb[ks] : q_lds(ks), ks ? s[kb] : zero16, 0, 0, 0);
             }
     };
     // Exponentials of a tile's scores alone (last tile of a wavefront).
@@ -852,29 +885,32 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
         return cross_half_max(mx);
     };
     // A(t): exponentials of S(t-1) (VALU) interleaved with the MFMAs of S(t),
-    // one chunk per k-step; the compiler may reorder only inside a chunk.
+    // one chunk per k-step (EP / KS pairs each: 2 at head_dim 128, one every
+    // other k-step at 256); the compiler may reorder only inside a chunk.
     auto a_full = [&](auto sk, float16_t (&sn)[KB], const float16_t (&so)[KB]) {
         const bf16_t *Ks = kst(sk);
         const float nref = -m_run;
         float lsum = 0.f;
         uint32_t pk[NE / 2];
-        // K operands KPF k-steps ahead.
-        short8_t ka[KPF + 1][KB];
-        auto read_k = [&](int ks, short8_t (&dst)[KB]) {
+        // K operands (and the Q^T operands held in LDS) KPF k-steps ahead.
+        short8_t ka[KPF + 1][KB], qa[KPF + 1];
+        auto read_k = [&](int ks, short8_t (&dst)[KB], short8_t &qdst) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) dst[kb] = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff(ks));
+            if (ks >= KQR) qdst = q_lds(ks);
         };
 #pragma unroll
-        for (int ks = 0; ks < KPF; ++ks) read_k(ks, ka[ks]);
+        for (int ks = 0; ks < KPF; ++ks) read_k(ks, ka[ks], qa[ks]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + KPF < KS) read_k(ks + KPF, ka[(ks + KPF) % (KPF + 1)]);
+            if (ks + KPF < KS) read_k(ks + KPF, ka[(ks + KPF) % (KPF + 1)], qa[(ks + KPF) % (KPF + 1)]);
+            const short8_t qop = ks < KQR ? qb[ks] : qa[ks % (KPF + 1)];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (KPF + 1)][kb], qb[ks], ks ? sn[kb] : zero16, 0, 0, 0);
+                sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (KPF + 1)][kb], qop, ks ? sn[kb] : zero16, 0, 0, 0);
 #pragma unroll
-            for (int x = 0; x < EA; x += 2) {
-                const int e = ks * EA + x;
+            for (int x = ks * EP / KS; x < (ks + 1) * EP / KS; ++x) {
+                const int e = 2 * x;
                 const float a = fast_exp2(fmaf(so[e / 16][e % 16], sl2, nref));
                 const float b = fast_exp2(fmaf(so[(e + 1) / 16][(e + 1) % 16], sl2, nref));
                 pk[e / 2] = cvt_pk_bf16(a, b);
@@ -1039,7 +1075,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 template <int D>
 hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
                             hipStream_t stream) {
-    if constexpr (D <= 128 && RA_PREFILL_PINGPONG) {
+    if constexpr ((D <= 128 && RA_PREFILL_PINGPONG) || (D == 256 && RA_PREFILL_PP256)) {
         hipLaunchKernelGGL(prefill_pp_kernel<D>, dim3(plan.n_prefill_items), dim3(PingPongCfg<D>::NTHR), 0,
                            stream, p, items, self_plan ? 1 : 0, plan.q_tile);
         return hipGetLastError();
@@ -1068,7 +1104,7 @@ int prefill_rows(int D) {
     switch (D) {
         case 64: return RA_PREFILL_PINGPONG ? PingPongCfg<64>::ROWS : PrefillCfg<64>::ROWS;
         case 128: return RA_PREFILL_PINGPONG ? PingPongCfg<128>::ROWS : PrefillCfg<128>::ROWS;
-        case 256: return PrefillCfg<256>::ROWS;
+        case 256: return RA_PREFILL_PP256 ? PingPongCfg<256>::ROWS : PrefillCfg<256>::ROWS;
         default: return 0;
     }
 }
