@@ -163,7 +163,7 @@ def ingest_counters(args):
     fetch, write = counter_means(fetch_dir, "FETCH_SIZE"), counter_means(write_dir, "WRITE_SIZE")
     path = os.path.join(ROOT, "profiles", "traffic.json")
     db = json.load(open(path)) if os.path.exists(path) else {}
-    for stage, knames in (("decode", ("decode_kernel",)), ("prefill", ("prefill_pp_kernel", "prefill_kernel"))):
+    for stage, knames in (("decode", ("decode_kernel",)), ("prefill", ("prefill_pp_kernel",))):
         keys = [k for k in fetch if k.split("<")[0].split("(")[0].strip() in knames]
         if not keys:
             continue
@@ -480,8 +480,7 @@ def main():
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                 "traffic": measured_traffic("prefill", args.config),
-                "kernel": ("generic_kernel" if args.variant == "generic" else
-                           "prefill_pp_kernel" if b.head_dim <= 128 else "prefill_kernel"),
+                "kernel": "generic_kernel" if args.variant == "generic" else "prefill_pp_kernel",
                 "algorithmic_flops_per_launch": units, "kernel_us": kern_s * 1e6}
 
     if pre and not dec:

@@ -1,32 +1,30 @@
-// prefill.hip -- the MFMA-bound kernels for prefill chunks (requests with more
-// than one new token), with the KV-cache update fused in.  head_dim 64 and
-// 128 run the two-group kernel further below (prefill_pp_kernel); head_dim
-// 256 runs prefill_kernel, described here.
+// prefill.hip -- the MFMA-bound kernel for prefill chunks (requests with more
+// than one new token), with the KV-cache update fused in (prefill_pp_kernel,
+// head_dim 64, 128 and 256).
 //
-// Work unit: one workgroup of NW wavefronts per (request r, kv head hk, query
-// tile of ROWS/G tokens), read from the plan kernel's item list or, for
+// Work unit: one workgroup of 8 wavefronts per (request r, kv head hk, query
+// tile of 256/G tokens), read from the plan kernel's item list or, for
 // batches of at most kSelfPlanReqs requests, found by the workgroup itself
-// (self_plan_prefill_item).  Its ROWS query rows are the G query heads of the
+// (self_plan_prefill_item).  Its 256 query rows are the G query heads of the
 // group times the tile's tokens, so one K/V tile in LDS serves every head
-// that reads it (grouped-query attention).  Wavefront w owns MW consecutive
-// rows (two 32-row halves when MW = 64): each K or V element it reads from
-// LDS feeds two MFMAs, which halves the LDS traffic per FLOP.
+// that reads it (grouped-query attention); wavefront w owns rows 32 w ..
+// 32 w + 31.
 //
-// Key tiles of N keys (32 or 64) stream through a ring of NSTAGE LDS stages with
-// direct-to-LDS 16-byte loads (global_load_lds_dwordx4): no registers hold
-// data in flight, and NSTAGE - 1 tiles are in flight while one is used.  In
-// one tile every wavefront loads N/4 key rows (inside one page of the paged
-// cache, so their page id is one scalar load); lane l of a 1 KiB load lands at byte
-// 16 l, and each lane fetches the chunk that makes the LDS layout XOR
-// swizzled (chunk c of row j at position c ^ (j & SWM)), so the MFMA-layout
-// reads below are free of bank conflicts.  Keys at positions < c_r come from
-// the cache through the page table, positions >= c_r from k_new/v_new;
-// positions past the tile's last visible key read that key again (finite,
-// and masked).
+// Key tiles of N keys (64, or 32 at head_dim 256) stream through four LDS
+// stages with direct-to-LDS 16-byte loads (global_load_lds_dwordx4): no
+// registers hold data in flight.  Each loading wavefront fetches N/4 key rows
+// of a tile (inside one 16-row block of a cache page, so their page id is one
+// scalar load); lane l of a 1 KiB load lands at byte 16 l, and each lane
+// fetches the chunk that makes the LDS layout XOR swizzled (K chunk c of row
+// j at position c ^ (j & SWM)), so the MFMA-layout reads below are free of
+// bank conflicts.  Keys at positions < c_r come from the cache through the
+// page table, positions >= c_r from k_new/v_new; positions past the tile's
+// last visible key read that key again (finite, and masked).
 //
 // Per tile and wavefront (v_mfma_f32_32x32x16_bf16 throughout):
 //   S^T[key][row] = K . Q^T     A = K rows from LDS (16 B per lane),
-//                               B = Q^T held in registers for the whole loop;
+//                               B = Q^T held in registers for the whole loop
+//                               (its last four k-steps in LDS at head_dim 256);
 //   online softmax on S^T       each lane owns one query row: the row max is
 //                               an in-lane max plus one cross-half step; the
 //                               scale is folded into one FMA before exp2; the
@@ -94,464 +92,16 @@ constexpr float kLazyLog2 = 8.f;
 // this wavefront are outstanding (expcnt and lgkmcnt left at their maximum).
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// Tile shape per head_dim: wavefronts per workgroup (NW), keys per tile (N),
-// LDS ring depth (NSTAGE), workgroups resident per CU (OCC) and query rows
-// per wavefront (MW: 32, or 64 as two halves that share every K/V read).
-// LDS operand prefetch depth of the two-group kernel.
+// LDS operand prefetch depth of the prefill kernel.
 #ifndef RA_PP_KPF
 #define RA_PP_KPF 2
 #endif
 #ifndef RA_PP_VPF
 #define RA_PP_VPF 2
 #endif
-// 1: head_dim 64 / 128 use the two-group kernel (prefill_pp_kernel).
-#ifndef RA_PREFILL_PINGPONG
-#define RA_PREFILL_PINGPONG 1
-#endif
-// 1: head_dim 256 uses it too.
-#ifndef RA_PREFILL_PP256
-#define RA_PREFILL_PP256 1
-#endif
-
-template <int D>
-struct PrefillShape;
-#ifndef RA_PREFILL_MW128
-#define RA_PREFILL_MW128 32
-#endif
-#ifndef RA_PREFILL_NW128
-#define RA_PREFILL_NW128 8
-#endif
-#ifndef RA_PREFILL_N128
-#define RA_PREFILL_N128 64
-#endif
-template <>
-struct PrefillShape<64> {
-    static constexpr int MW = 32, NW = 8, N = 64, NSTAGE = 4, OCC = 1;
-};
-template <>
-struct PrefillShape<128> {
-    static constexpr int MW = RA_PREFILL_MW128, NW = RA_PREFILL_NW128, N = RA_PREFILL_N128,
-                         NSTAGE = 4, OCC = 1;
-};
-template <>
-struct PrefillShape<256> {
-    static constexpr int MW = 32, NW = 4, N = 32, NSTAGE = 4, OCC = 1;
-};
-
-template <int D>
-struct PrefillCfg {
-    using S = PrefillShape<D>;
-    static constexpr int MW = S::MW;                // query rows per wavefront
-    static constexpr int NH = MW / 32;              // 32-row halves per wavefront
-    static constexpr int NW = S::NW;                // wavefronts per workgroup
-    static constexpr int N = S::N;                  // keys per tile
-    static constexpr int OCC = S::OCC;              // workgroups per CU (launch bound)
-    static constexpr int NTHR = 64 * NW;
-    static constexpr int ROWS = NW * MW;            // query rows per workgroup
-    static constexpr int KB = N / 32;               // 32-key blocks of S^T
-    static constexpr int KS = D / 16;               // 16-dim k-steps of QK^T
-    static constexpr int MD = D / 32;               // 32-dim blocks of O^T
-    static constexpr int CPR = D / 8;               // 16-byte chunks per K/V row
-    static constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;  // K chunk swizzle mask
-    static constexpr int VSS = CPR >= 16 ? 4 : 2;   // V chunk swizzle step
-    static constexpr int TILE = N * D;              // elements of one K (or V) tile
-    static constexpr int NSTAGE = S::NSTAGE;        // LDS ring depth
-    static constexpr int RW = N / NW;               // key rows each wavefront loads per tile
-    static constexpr int RPI = 64 / CPR;            // rows per 1 KiB wavefront load
-    static constexpr int IPW = RW / RPI;            // loads per wavefront per tensor and tile
-    static constexpr size_t LDS_BYTES = (size_t)NSTAGE * 2 * TILE * sizeof(bf16_t);
-    static_assert(16 % RW == 0 && RW % RPI == 0 && IPW >= 1, "a wavefront's rows of a tile lie in one page");
-};
-
-template <int D>
-__global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefill_kernel(
-    Params p, const int4 *__restrict__ items, int self_plan, int q_tile) {
-    using C = PrefillCfg<D>;
-    constexpr int NH = C::NH, ROWS = C::ROWS, N = C::N, KB = C::KB, KS = C::KS, MD = C::MD,
-                  CPR = C::CPR, SWM = C::SWM, TILE = C::TILE, NSTAGE = C::NSTAGE, RW = C::RW,
-                  RPI = C::RPI, IPW = C::IPW, NTHR = C::NTHR, VSS = C::VSS, MW = C::MW;
-    static_assert(NSTAGE >= 4, "tile t+1 is computed on while tile t+2 is in flight");
-    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-    // smem: NSTAGE stages of [K tile | V tile], each tile N rows x D, swizzled
-
-    int4 it, it2;
-    if (self_plan) {
-        self_plan_prefill_item(p, blockIdx.x, q_tile, it, it2);
-    } else {
-        it = items[2 * blockIdx.x];
-        it2 = items[2 * blockIdx.x + 1];
-    }
-    const int r = it.x;
-    if (r < 0) return;
-    const int hk = it.y, q0 = it.z, t0 = it.w, c = it2.x, qlen = it2.y;
-    const int tid = threadIdx.x;
-    // The wavefront index as a scalar (the compiler cannot see that tid >> 6
-    // is uniform), so that per-wavefront metadata loads are scalar loads.
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l = tid & 63, n32 = l & 31, h2 = l >> 5;
-    const int Hq = p.Hq, Hkv = p.Hkv, G = Hq / Hkv, QT = ROWS / G;
-    const int L = c + qlen;
-    const int tile_q = min(QT, qlen - q0);
-    const int kv_end = p.causal ? c + q0 + tile_q : L;  // keys 0 .. kv_end-1 are visible to someone
-    const int ntiles = (kv_end + N - 1) / N;
-    const size_t prow = (size_t)r * p.max_pages;
-
-    // Fused KV-cache update: the new rows of this tile's tokens, kv head hk.
-    for (int idx = tid; idx < (p.skip_scatter ? 0 : tile_q * CPR); idx += NTHR) {
-        const int row = idx / CPR, col = idx - row * CPR;
-        const int t = t0 + q0 + row;
-        const size_t dst = ((size_t)ld_meta(p.slot_mapping, t) * Hkv + hk) * D + 8 * col;
-        const size_t src = ((size_t)t * Hkv + hk) * D + 8 * col;
-        *reinterpret_cast<uint4 *>(p.k_cache + dst) = *reinterpret_cast<const uint4 *>(p.k_new + src);
-        *reinterpret_cast<uint4 *>(p.v_cache + dst) = *reinterpret_cast<const uint4 *>(p.v_new + src);
-    }
-
-    // This lane's query rows, one per half h: row R = MW w + 32 h + n32 is
-    // head g = R / QT, token i = R % QT of the tile.
-    int gh[NH], qi[NH], lim[NH];
-    bool rvalid[NH];
-    short8_t qb[NH][KS];
-    int lim_max = -1, lim_min = 0x7fffffff;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const int R = MW * w + 32 * h + n32;
-        gh[h] = R / QT;
-        const int iq = R - gh[h] * QT;
-        rvalid[h] = iq < tile_q;
-        qi[h] = q0 + (rvalid[h] ? iq : 0);
-        lim[h] = rvalid[h] ? (p.causal ? c + qi[h] : L - 1) : -1;  // last visible key
-        lim_max = max(lim_max, lim[h]);
-        if (rvalid[h]) lim_min = min(lim_min, lim[h]);
-        // Q^T as the B operand: lane holds q[t0 + qi][hk*G + g][16ks + 8h2 .. +8].
-        const bf16_t *qrow = p.q + ((size_t)(t0 + qi[h]) * Hq + hk * G + gh[h]) * D + 8 * h2;
-        const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const short8_t x = *reinterpret_cast<const short8_t *>(qrow + 16 * ks);
-            qb[h][ks] = rvalid[h] ? x : z;
-        }
-    }
-    const int wave_end = wave_max_i(lim_max + 1);  // keys this wavefront needs
-    const int wave_lim_min = wave_min_i(lim_min);
-    const int ntw = min(ntiles, (wave_end + N - 1) / N);  // tiles this wavefront computes
-
-    // Direct-to-LDS loads of tile `tile` into stage `stage`: wavefront w loads
-    // key rows RW w .. RW w + RW - 1 (inside one page) of the K and V tiles.
-    const int lrow = l / CPR, lpc = l - lrow * CPR;  // row inside a 1 KiB load, physical chunk
-    // K tiles: chunk c of row j sits at c ^ (j & SWM), so that the 16 rows a
-    // 16-lane group reads with ds_read_b128 hit 16 different bank groups.  V
-    // tiles: chunk c of row j sits at c ^ VSS (j & 3), so that the 4 rows x
-    // 2 chunks a 16-lane group reads with ds_read_b64_tr_b16 (and the next
-    // group's 2 chunks) hit different banks; every read of a lane then sits
-    // at a fixed per-lane offset plus an immediate.
-    auto v_swizzle = [](int row) { return ((row & 3) * VSS) & SWM; };
-    // The four tensor bases as values (a select between struct fields could
-    // become a load of the field, which would wait for every load in flight).
-    const bf16_t *const kcache = p.k_cache, *const vcache = p.v_cache;
-    const bf16_t *const knew = p.k_new + (size_t)t0 * Hkv * D, *const vnew = p.v_new + (size_t)t0 * Hkv * D;
-    auto load_tile = [&](int tile, int stage) {
-        const int jw = tile * N + RW * w;                 // first key row of this wavefront
-        const int jp = min(jw, kv_end - 1);               // a visible position of the same page
-        const size_t page = (size_t)ld_meta(p.page_table, prow + jp / p.S);
-        bf16_t *kst = smem + stage * 2 * TILE + RW * w * D;
-#pragma unroll
-        for (int u = 0; u < IPW; ++u) {
-            const int kr = RPI * u + lrow;                // row inside the wavefront's RW
-            const int j = min(jw + kr, kv_end - 1);       // rows past the end repeat the last key
-            const int row = RW * w + kr;                  // row inside the tile
-            const int lk = lpc ^ (row & SWM);             // logical K chunk landing at lpc
-            const int lv = lpc ^ v_swizzle(row);          // logical V chunk landing at lpc
-            const size_t crow = ((page * p.S + j % p.S) * Hkv + hk) * D;
-            const size_t nrow = ((size_t)(j - c) * Hkv + hk) * D;
-            const bool cached = j < c;
-            load_lds16((cached ? kcache + crow : knew + nrow) + 8 * lk, kst + RPI * u * D);
-            load_lds16((cached ? vcache + crow : vnew + nrow) + 8 * lv, kst + TILE + RPI * u * D);
-        }
-    };
-
-    // Per-lane LDS offsets (elements) of the MFMA-layout reads, fixed for the
-    // whole loop: K row n32 (+ 32 kb), dim chunk 2ks + h2; V^T rows
-    // 4h2 + (l & 15) / 4 (+ 16 s16, + 8 for the upper 4 keys), dims
-    // 32md + 16 (n32 / 16) + 4 (l & 3) .. +4.
-    int koff[KS], voff[MD];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) koff[ks] = n32 * D + 8 * ((2 * ks + h2) ^ (n32 & SWM));
-    {
-        const int vr0 = 4 * h2 + ((l & 15) >> 2);
-        const int vc = 16 * (n32 >> 4) + 4 * (l & 3);
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-            const int col = 32 * md + vc;
-            voff[md] = vr0 * D + 8 * ((col >> 3) ^ v_swizzle(vr0)) + (col & 7);
-        }
-    }
-    const float16_t zero16 = {};
-    const float sl2 = p.scale_log2;
-
-    float16_t o[NH][MD];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int md = 0; md < MD; ++md) o[h][md] = zero16;
-    float m_run[NH], l_run[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        m_run[h] = -INFINITY;
-        l_run[h] = 0.f;
-    }
-
-    constexpr int NE = KB * 16;            // scores per lane, half and tile
-    // Element e of a half's scores is s[e / 16][e % 16], key
-    // 32 (e / 16) + 8 ((e % 16) / 4) + 4 h2 + e % 4 of the tile.
-    auto key_of = [](int e) { return 32 * (e / 16) + 8 * ((e % 16) >> 2) + (e & 3); };
-
-    // S^T[key][row] = K . Q^T for the tile in `stage`; each K read feeds
-    // every half.
-    auto qk = [&](int stage, float16_t (&s)[NH][KB]) {
-        const bf16_t *Ks = smem + stage * 2 * TILE;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const short8_t a = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff[ks]);
-#pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    s[h][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[h][ks], ks ? s[h][kb] : zero16, 0, 0, 0);
-            }
-    };
-    // Row max (scaled) of tile `tile` for half h, masking keys past the row's
-    // last one when MASKED.
-    auto rowmax = [&](auto masked, int tile, int h, float16_t (&s)[KB]) {
-        if constexpr (decltype(masked)::value) {
-            const int thr = lim[h] - tile * N - 4 * h2;  // key offset past which keys are masked
-#pragma unroll
-            for (int e = 0; e < NE; ++e)
-                s[e / 16][e % 16] = key_of(e) > thr ? -INFINITY : s[e / 16][e % 16];
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < NE; e += 2) mx = fmaxf(fmaxf(mx, s[e / 16][e % 16]), s[e / 16][e % 16 + 1]);
-        return fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;  // raw max, then scaled (scale > 0)
-    };
-    // Lazy rescale: the reference max moves only when a row max exceeds it by
-    // more than kLazyLog2 (P <= 2^kLazyLog2 otherwise).
-    auto rescale = [&](int h, float mx) {
-        if (__builtin_amdgcn_ballot_w64(mx > m_run[h] + kLazyLog2)) {
-            const float mn = fmaxf(m_run[h], mx);
-            const float alpha = fast_exp2(m_run[h] - mn);
-            l_run[h] *= alpha;
-#pragma unroll
-            for (int md = 0; md < MD; ++md) o[h][md] *= alpha;
-            m_run[h] = mn;
-        }
-    };
-    auto masked_tile = [&](int tile) { return tile * N + N - 1 > wave_lim_min; };
-    // P^T = exp2(S^T * scale - m) of half h as bf16 B operands; returns the
-    // lane's sum of those bf16 values (the row sum is taken over the same
-    // rounded P that the PV product uses, so the weights sum to one).
-    auto pack = [&](const float (&pe)[NE], short8_t (&pb)[N / 16]) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int s16 = 0; s16 < N / 16; ++s16) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                w4[e2] = cvt_pk_bf16(pe[8 * s16 + 2 * e2], pe[8 * s16 + 2 * e2 + 1]);
-                lsum = pair_sum_bf16(w4[e2], lsum);
-            }
-            pb[s16] = __builtin_bit_cast(short8_t, w4);
-        }
-        return lsum;
-    };
-    auto tail = [&](int h, const float16_t (&s)[KB], short8_t (&pb)[N / 16]) {
-        const float nref = -m_run[h];
-        float pe[NE];
-#pragma unroll
-        for (int e = 0; e < NE; ++e) pe[e] = fast_exp2(fmaf(s[e / 16][e % 16], sl2, nref));
-        l_run[h] += pack(pe, pb);
-    };
-    // O^T += V^T . P^T over the tile in `stage`, 16 keys per MFMA; each V^T
-    // read feeds every half.
-    auto pv = [&](int stage, const short8_t (&pb)[NH][N / 16]) {
-        const bf16_t *Vs = smem + stage * 2 * TILE + TILE;
-#pragma unroll
-        for (int s16 = 0; s16 < N / 16; ++s16)
-#pragma unroll
-            for (int md = 0; md < MD; ++md) {
-                const bf16_t *v = Vs + 16 * s16 * D + voff[md];
-                const short4_t lo = lds_read_tr16(v);
-                const short4_t hi = lds_read_tr16(v + 8 * D);
-                const short8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    o[h][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h][s16], o[h][md], 0, 0, 0);
-            }
-    };
-
-    // One pipelined iteration, hand-interleaved in chunks that the compiler
-    // may reorder only internally (sched_barrier between chunks):
-    //   phase A, one chunk per k-step: the K reads for the next k-step, the
-    //     MFMAs of tile t+1's scores for this k-step, and a share of tile t's
-    //     exponentials (VALU);
-    //   phase B, one chunk per (16-key step, 32-dim block): the V^T reads for
-    //     the next chunk, the MFMAs of tile t's P.V, and a share of tile t+1's
-    //     (masked) row max.
-    // MFMAs are asynchronous, so the VALU work of each chunk runs while the
-    // chunk's MFMAs occupy the matrix unit.
-    float16_t s_cur[NH][KB];                // scores of the tile being finished
-    constexpr int EA = NH * NE / KS;        // exponentials per phase-A chunk
-    constexpr int NB = (N / 16) * MD;       // phase-B chunks
-    constexpr int EB = NH * NE / NB;        // row-max elements per phase-B chunk
-    static_assert((NH * NE) % KS == 0 && (NH * NE) % NB == 0, "chunks must split the scores evenly");
-    auto step = [&](auto masked, int t, float16_t (&s_nxt)[NH][KB], short8_t (&pb)[NH][N / 16],
-                    float (&mx)[NH]) {
-        const bf16_t *Ks = smem + ((t + 1) % NSTAGE) * 2 * TILE;
-        const bf16_t *Vs = smem + (t % NSTAGE) * 2 * TILE + TILE;
-        // ---- phase A
-        float nref[NH], pe[NH][NE];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            nref[h] = -m_run[h];
-        }
-        short8_t ka[2][KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) ka[0][kb] = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff[0]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    ka[(ks + 1) & 1][kb] = *reinterpret_cast<const short8_t *>(Ks + 32 * kb * D + koff[ks + 1]);
-            }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int h = 0; h < NH; ++h)
-                    s_nxt[h][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb], qb[h][ks],
-                                                                           ks ? s_nxt[h][kb] : zero16, 0, 0, 0);
-#pragma unroll
-            for (int x = 0; x < EA; ++x) {
-                const int f = ks * EA + x, h = f / NE, e = f % NE;
-                pe[h][e] = fast_exp2(fmaf(s_cur[h][e / 16][e % 16], sl2, nref[h]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            l_run[h] += pack(pe[h], pb[h]);
-        }
-        // ---- phase B
-        int thr[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            thr[h] = lim[h] - (t + 1) * N - 4 * h2;  // key offset past which tile t+1 is masked
-            mx[h] = -INFINITY;
-        }
-        short8_t va[2];
-        {
-            const short4_t lo = lds_read_tr16(Vs + voff[0]);
-            const short4_t hi = lds_read_tr16(Vs + voff[0] + 8 * D);
-            va[0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int s16 = j / MD, md = j % MD;
-            if (j + 1 < NB) {
-                const bf16_t *v = Vs + 16 * ((j + 1) / MD) * D + voff[(j + 1) % MD];
-                const short4_t lo = lds_read_tr16(v);
-                const short4_t hi = lds_read_tr16(v + 8 * D);
-                va[(j + 1) & 1] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-#pragma unroll
-            for (int h = 0; h < NH; ++h)
-                o[h][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j & 1], pb[h][s16], o[h][md], 0, 0, 0);
-#pragma unroll
-            for (int x = 0; x < EB; ++x) {
-                const int f = j * EB + x, h = f / NE, e = f % NE;
-                float v = s_nxt[h][e / 16][e % 16];
-                if constexpr (decltype(masked)::value) {
-                    v = key_of(e) > thr[h] ? -INFINITY : v;
-                    s_nxt[h][e / 16][e % 16] = v;
-                }
-                mx[h] = fmaxf(mx[h], v);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int h = 0; h < NH; ++h) mx[h] = fmaxf(mx[h], __shfl_xor(mx[h], 32, 64)) * sl2;
-    };
-
-    // Prologue: NSTAGE - 1 tiles in flight (tiles past the end reload the last
-    // one, so that every path issues the same loads and the wait counts below
-    // stay exact); tile 0's scores and their row max.
-#pragma unroll
-    for (int st = 0; st < NSTAGE - 1; ++st) load_tile(min(st, ntiles - 1), st);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * IPW * (NSTAGE - 2)));
-    __syncthreads();
-    if (ntw > 0) {
-        qk(0, s_cur);
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-            const float mx = masked_tile(0) ? rowmax(std::true_type(), 0, h, s_cur[h])
-                                             : rowmax(std::false_type(), 0, h, s_cur[h]);
-            rescale(h, mx);
-        }
-    }
-
-    // Software pipeline, one tile per iteration (see step).
-    for (int t = 0; t < ntiles; ++t) {
-        // Tile t+1 must be in LDS; tiles t+2 .. t+NSTAGE-2 may stay in flight.
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * IPW * (NSTAGE - 3)));
-        __syncthreads();
-        // Tile t-1's stage is free now (everyone finished its P.V): refill it.
-        load_tile(min(t + NSTAGE - 1, ntiles - 1), (t + NSTAGE - 1) % NSTAGE);
-        if (t < ntw) {
-            short8_t pb[NH][N / 16];
-            if (t + 1 < ntw) {
-                float16_t s_nxt[NH][KB];
-                float mx[NH];
-                if (masked_tile(t + 1)) {
-                    step(std::true_type(), t, s_nxt, pb, mx);
-                } else {
-                    step(std::false_type(), t, s_nxt, pb, mx);
-                }
-#pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    rescale(h, mx[h]);
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) s_cur[h][kb] = s_nxt[h][kb];
-                }
-            } else {
-#pragma unroll
-                for (int h = 0; h < NH; ++h) tail(h, s_cur[h], pb[h]);
-                pv(t % NSTAGE, pb);
-            }
-        }
-    }
-    // No direct-to-LDS load may still be writing when the workgroup retires.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const float l_tot = l_run[h] + __shfl_xor(l_run[h], 32, 64);
-        if (!rvalid[h]) continue;
-        const float inv = 1.f / l_tot;
-        bf16_t *orow = p.out + ((size_t)(t0 + qi[h]) * Hq + hk * G + gh[h]) * D;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                uint2 v;
-                v.x = cvt_pk_bf16(o[h][md][4 * q4] * inv, o[h][md][4 * q4 + 1] * inv);
-                v.y = cvt_pk_bf16(o[h][md][4 * q4 + 2] * inv, o[h][md][4 * q4 + 3] * inv);
-                *reinterpret_cast<uint2 *>(orow + 32 * md + 8 * q4 + 4 * h2) = v;
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
-// Two-group kernel for head_dim 64 and 128.
+// Two groups.
 //
 // The eight wavefronts form two groups, waves 0-3 and waves 4-7, one wave of
 // each per SIMD.  Per key tile a wavefront runs two phases:
@@ -564,7 +114,7 @@ __global__ __launch_bounds__(PrefillCfg<D>::NTHR, PrefillCfg<D>::OCC) void prefi
 //
 // Tile t lives in LDS stage t % 4 (separate K and V arrays per stage).  Group
 // 0 issues the direct-to-LDS loads of tile t+2 at the start of its B(t) --
-// one page of 16 key rows per wavefront -- and waits for tile t+1 at its end;
+// N/4 key rows per wavefront -- and waits for tile t+1 at its end;
 // by then every reader of the stage's previous tile (t-2) has passed a
 // barrier.  The loop is unrolled by the four stages so that every LDS access
 // names its stage array at compile time; the compiler can then tell the
@@ -1075,22 +625,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 template <int D>
 hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
                             hipStream_t stream) {
-    if constexpr ((D <= 128 && RA_PREFILL_PINGPONG) || (D == 256 && RA_PREFILL_PP256)) {
-        hipLaunchKernelGGL(prefill_pp_kernel<D>, dim3(plan.n_prefill_items), dim3(PingPongCfg<D>::NTHR), 0,
-                           stream, p, items, self_plan ? 1 : 0, plan.q_tile);
-        return hipGetLastError();
-    }
-    using C = PrefillCfg<D>;
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
-    const size_t lds = C::LDS_BYTES;
-    hipLaunchKernelGGL(prefill_kernel<D>, dim3(plan.n_prefill_items), dim3(C::NTHR), lds, stream, p, items,
-                       self_plan ? 1 : 0, plan.q_tile);
+    hipLaunchKernelGGL(prefill_pp_kernel<D>, dim3(plan.n_prefill_items), dim3(PingPongCfg<D>::NTHR), 0, stream,
+                       p, items, self_plan ? 1 : 0, plan.q_tile);
     return hipGetLastError();
 }
 
@@ -1102,9 +638,9 @@ bool prefill_supports(int D, int G) {
 
 int prefill_rows(int D) {
     switch (D) {
-        case 64: return RA_PREFILL_PINGPONG ? PingPongCfg<64>::ROWS : PrefillCfg<64>::ROWS;
-        case 128: return RA_PREFILL_PINGPONG ? PingPongCfg<128>::ROWS : PrefillCfg<128>::ROWS;
-        case 256: return RA_PREFILL_PP256 ? PingPongCfg<256>::ROWS : PrefillCfg<256>::ROWS;
+        case 64: return PingPongCfg<64>::ROWS;
+        case 128: return PingPongCfg<128>::ROWS;
+        case 256: return PingPongCfg<256>::ROWS;
         default: return 0;
     }
 }
