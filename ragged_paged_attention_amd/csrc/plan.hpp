@@ -13,6 +13,8 @@
 // log-sum-exp combines the partial (m, l, o) of its workgroups.
 //
 // Prefill: chunks are cut into query tiles of `q_tile` tokens per kv head.
+// Self-planned batches hand the items out longest first across requests
+// (self_plan_prefill_item); the plan kernel writes them request by request.
 //
 // The host computes counts and the workspace layout only.  Batches of at
 // most kSelfPlanReqs requests need no further planning: the decode and
@@ -36,51 +38,133 @@ namespace ra {
 // wave scan over the requests; larger batches run the plan kernel.
 constexpr int kSelfPlanReqs = 512;
 
-// Prefill item k of a batch of at most kSelfPlanReqs requests, found
-// without the plan kernel: the item the plan kernel would
-// write at position k (requests in order; per request its query tiles,
-// longest key range first, each for every kv head).  Every lane of the
-// calling wavefront must take part: lane l holds requests l, l + 64, ...
-// (one round trip of loads) and a wave scan of their item counts finds the
-// request of item k.
-__device__ __forceinline__ void self_plan_prefill_item(const Params &p, int k, int q_tile, int4 &it,
-                                                       int4 &it2) {
-    constexpr int KR = kSelfPlanReqs / 64;
-    const int lane = threadIdx.x & 63, R = p.R;
-    int q[KR];
+// Sum (or max) over the wavefront, the same in every lane: DPP within each
+// row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror), then the four row results read as scalars.
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_i(int x) {
+    auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };
+    x = op(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+    x = op(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+    x = op(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false));
+    x = op(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false));
+    return op(op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+              op(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Prefill item k of a batch of KR * 64 requests at most, found without the
+// plan kernel.  Items go out longest first: in decreasing order of the key
+// tiles (key_tile keys each) they read, ties in request order, then rank
+// (query tile from the last one back), then kv head.  The hardware starts
+// workgroups in index order as compute units free up, so this is
+// longest-processing-time-first scheduling across all requests.  Every lane
+// of the calling wavefront must take part: lane l holds requests l, l + 64,
+// ... (one round trip of loads); a binary search over the tile count, each
+// step a wave sum of per-request counts in closed form, finds the tile count
+// of item k, and a wave scan finds its request, whose metadata the owning
+// lane already holds.  q_tile must be a power of two.  A result that falls
+// outside the batch (not expected) turns the item into a no-op (it.x = -1).
+template <int KR>
+__device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k, int q_tile, int key_tile,
+                                                         int4 &it, int4 &it2) {
+    const int lane = threadIdx.x & 63, R = p.R, Hkv = p.Hkv;
+    const int qsh = __builtin_ctz(q_tile);
+    int t0s[KR], q[KR], c[KR], nt[KR];
+    int tmax = 0;
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
         const int r = 64 * j + lane;
-        q[j] = r < R ? p.cu_q_lens[r + 1] - p.cu_q_lens[r] : 0;
+        t0s[j] = r < R ? p.cu_q_lens[r] : 0;
+        const int qr = r < R ? p.cu_q_lens[r + 1] - t0s[j] : 0;
+        q[j] = qr > 1 ? qr : 0;  // decode and empty requests have no prefill items
+        c[j] = r < R ? p.context_lens[r] : 0;
+        nt[j] = (q[j] + q_tile - 1) >> qsh;
+        if (q[j]) tmax = max(tmax, (c[j] + q[j] + key_tile - 1) / key_tile);
     }
-    int base = 0, hit_r = 0, hit_excl = 0;
+    tmax = wave_reduce_i<true>(tmax);
+    // Ranks of request slot j whose key range ends at or past key x - 1 (at
+    // least x keys visible to the tile's last row): rank 0 (the last query
+    // tile) ends at c + q, rank rho >= 1 at c + (nt - rho) q_tile; without
+    // the causal mask every rank ends at c + q.
+    auto cnt_ge = [&](int j, int x) {
+        if (q[j] == 0 || c[j] + q[j] < x) return 0;
+        const int a = x - c[j];
+        if (!p.causal || a <= 0) return nt[j];
+        return 1 + max(0, min(nt[j] - 1, nt[j] - ((a + q_tile - 1) >> qsh)));
+    };
+    // Items that read at least lam key tiles.
+    auto at_least = [&](int lam) {
+        const int x = (lam - 1) * key_tile + 1;
+        int s = 0;
+#pragma unroll
+        for (int j = 0; j < KR; ++j)
+            if (64 * j < R) s += cnt_ge(j, x);
+        return wave_reduce_i<false>(s) * Hkv;
+    };
+    // Largest lam with more than k items reading at least lam tiles.
+    int lo = 1, hi = tmax + 1;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (at_least(mid) > k) lo = mid;
+        else hi = mid;
+    }
+    const int m = k - at_least(lo + 1);  // position among the items of exactly lo tiles
+    const int x_eq = (lo - 1) * key_tile + 1, x_more = lo * key_tile + 1;
+    int base = 0, hit_j = -1, hit_ln = 0, hit_excl = 0, hit_rank0 = 0;
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
         if (64 * j >= R) break;
         const int r = 64 * j + lane;
-        const int n = q[j] > 1 ? (q[j] + q_tile - 1) / q_tile * p.Hkv : 0;
+        const int longer = cnt_ge(j, x_more);
+        const int n = (cnt_ge(j, x_eq) - longer) * Hkv;
         int incl = n;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int t = __shfl_up(incl, off, 64);
             if (lane >= off) incl += t;
         }
-        const unsigned long long hit = __builtin_amdgcn_ballot_w64(r < R && base + incl > k);
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(r < R && base + incl > m);
         if (hit) {
-            const int ln = __builtin_ctzll(hit);
-            hit_r = 64 * j + ln;
-            hit_excl = __shfl(base + incl - n, ln, 64);
+            hit_ln = __builtin_ctzll(hit);
+            hit_j = j;
+            hit_excl = __builtin_amdgcn_readlane(base + incl - n, hit_ln);
+            hit_rank0 = __builtin_amdgcn_readlane(longer, hit_ln);
             break;
         }
-        base += __shfl(incl, 63, 64);
+        base += __builtin_amdgcn_readlane(incl, 63);
     }
-    const int r = __builtin_amdgcn_readfirstlane(hit_r);
-    const int local = k - __builtin_amdgcn_readfirstlane(hit_excl);
-    const int t0 = p.cu_q_lens[r], qr = p.cu_q_lens[r + 1] - t0;
-    const int ntiles = (qr + q_tile - 1) / q_tile;
-    const int rank = local / p.Hkv, hk = local - rank * p.Hkv;
+    const int j = __builtin_amdgcn_readfirstlane(hit_j);
+    const int ln = __builtin_amdgcn_readfirstlane(hit_ln);
+    const int local = m - __builtin_amdgcn_readfirstlane(hit_excl);
+    const int rank = __builtin_amdgcn_readfirstlane(hit_rank0) + local / Hkv, hk = local % Hkv;
+    // The request's metadata from the lane that holds it.
+    int t0v = 0, qv = 0, cv = 0;
+#pragma unroll
+    for (int jj = 0; jj < KR; ++jj)
+        if (jj == j) {
+            t0v = t0s[jj];
+            qv = q[jj];
+            cv = c[jj];
+        }
+    const int r = 64 * j + ln;
+    const int t0 = __builtin_amdgcn_readlane(t0v, ln), qr = __builtin_amdgcn_readlane(qv, ln);
+    const int ctx = __builtin_amdgcn_readlane(cv, ln);
+    const int ntiles = (qr + q_tile - 1) >> qsh;
+    if (j < 0 || r >= R || local < 0 || m < 0 || qr <= 1 || rank >= ntiles) {
+        it = make_int4(-1, 0, 0, 0);
+        it2 = make_int4(0, 0, 0, 0);
+        return;
+    }
     it = make_int4(r, hk, (ntiles - 1 - rank) * q_tile, t0);
-    it2 = make_int4(p.context_lens[r], qr, 0, 0);
+    it2 = make_int4(ctx, qr, 0, 0);
+}
+
+// As above for any batch of at most kSelfPlanReqs requests (one slot per
+// lane when there are at most 64).
+__device__ __forceinline__ void self_plan_prefill_item(const Params &p, int k, int q_tile, int key_tile,
+                                                       int4 &it, int4 &it2) {
+    if (p.R <= 64) self_plan_prefill_item_k<1>(p, k, q_tile, key_tile, it, it2);
+    else self_plan_prefill_item_k<kSelfPlanReqs / 64>(p, k, q_tile, key_tile, it, it2);
 }
 
 // Upper bound of decode workgroups per call (all head groups together); it

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
     // the prologue (new K/V rows, Q, the first two tiles) goes out at once.
     int4 it, it2;
     if (self_plan) {
-        self_plan_prefill_item(p, blockIdx.x, q_tile, it, it2);
+        self_plan_prefill_item(p, blockIdx.x, q_tile, N, it, it2);
     } else {
         it = items[2 * blockIdx.x];
         it2 = items[2 * blockIdx.x + 1];
