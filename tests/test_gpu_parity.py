@@ -227,6 +227,31 @@ def test_self_planned_prefill_matches_plan_kernel(D, monkeypatch):
     assert_close(out_self, ref, "self_plan_pre")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_longest_first_items_over_64_requests(causal, monkeypatch):
+    """200 requests (several per lane of the in-kernel planner): chunks of
+    2-90 tokens after 0-600 tokens of context, with decode and empty requests
+    among them.  The prefill items go out longest first; the plan kernel's
+    items (request order, RA_SELF_PLAN=0) give the same bits.  The decode
+    requests are short, which would give self-planned workgroups whole
+    requests (another split, so other rounding): RA_DECODE_WHOLE=0 keeps the
+    plan kernel's equal page ranges in both runs."""
+    monkeypatch.setenv("RA_DECODE_WHOLE", "0")
+    g = np.random.default_rng(83 + causal)
+    q = [int(x) for x in g.integers(0, 91, 200)]
+    q = [1 if x % 17 == 3 else x for x in q]
+    c = [int(x) for x in g.integers(0, 601, 200)]
+    b = build_batch(q, c, num_q_heads=8, num_kv_heads=2, head_dim=128, causal=causal, seed=83 + causal,
+                    name="longest_first_200")
+    out_self, kc_self, _ = run_gpu(b)
+    monkeypatch.setenv("RA_SELF_PLAN", "0")
+    out_plan, kc_plan, _ = run_gpu(b)
+    assert torch.equal(out_self.view(torch.int16), out_plan.view(torch.int16))
+    assert torch.equal(kc_self.view(torch.int16), kc_plan.view(torch.int16))
+    ref, _, _ = oracle_full(b)
+    assert_close(out_self, ref, "longest_first_200")
+
+
 def test_more_decode_requests_than_a_grid_dimension():
     """70000 decode requests (more than 65535: the merge kernel's grid puts
     requests on its x dimension) with short contexts, through the plan kernel;
