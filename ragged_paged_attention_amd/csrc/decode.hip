@@ -733,7 +733,7 @@ int decode_heads_per_group(int D, int Hkv, long long blocks, int nd) {
     return 1;
 }
 
-hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *nwg) {
+hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *nwg, int *fill, int *cus) {
     int cap = 0;
     hipError_t e;
     switch (p.D) {
@@ -743,6 +743,12 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
+    if (cus) {
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
     // One resident wave of workgroups, none with fewer than kMinPages pages.
     // RA_DECODE_WGS (environment) overrides the resident count, for tuning.
     constexpr int kMinPages = 4;
@@ -750,6 +756,7 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
     const int forced = env ? atoi(env) : 0;
     if (forced > 0) cap = forced * plan.decode_hgroups;
     int n = std::max(1, cap / plan.decode_hgroups);
+    if (fill) *fill = n;  // workgroups per head group that fill every compute unit once
     n = std::min(n, plan.decode_wg_cap);
     n = std::min(n, whole > 0 ? whole : std::max(1, plan.n_decode_pages / kMinPages));
     *nwg = n;

@@ -3,6 +3,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "launch.hpp"
@@ -241,6 +242,36 @@ hipError_t side_stream(SideStream **out) {
     return hipSuccess;
 }
 
+// The prefill items of a mixed batch start on the compute units the decode
+// kernel leaves free (nwg of its fill workgroups per head group hold
+// cus * nwg / fill units) and run in rounds of about one item per unit.
+// With only a few rounds a partial last round costs nearly a whole one, so
+// the split moves to the nearer of the two that end the items on whole
+// rounds, keeping the decode kernel on 40-90 % of the units.  (Mixed
+// workload, 96 decode requests and 512 prefill items: 0.53 of the units,
+// 4.2 rounds, 442 us per call; 0.5 and 0.6, 4 and 5 rounds, 430 us.)
+int whole_prefill_rounds(int nwg, int fill, int cus, int items) {
+    if (fill <= 0 || cus <= 0 || items <= 0 || nwg >= fill) return nwg;
+    const double dec = (double)cus * nwg / fill;  // units the decode kernel holds
+    const int free_units = cus - (int)dec;
+    if (free_units <= 0) return nwg;
+    const int rounds = (items + free_units - 1) / free_units;
+    if (rounds > 8) return nwg;  // the last of many rounds matters little
+    int best = nwg;
+    double best_d = 1e30;
+    for (int r = std::max(1, rounds - 1); r <= rounds; ++r) {
+        const int need = (items + r - 1) / r;  // units that run the items in r rounds
+        const int dec_units = cus - need;
+        if (dec_units < 0.4 * cus || dec_units > 0.9 * cus) continue;
+        const double d = std::fabs(dec_units - dec);
+        if (d < best_d) {
+            best_d = d;
+            best = std::max(1, (int)((long long)fill * dec_units / cus));
+        }
+    }
+    return best;
+}
+
 int env_int(const char *name, int dflt) {
     const char *v = getenv(name);
     return v ? atoi(v) : dflt;
@@ -282,11 +313,14 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     // kernel then leaves part of the compute units to it at first.
     const bool overlap = !ev.events && has_decode && has_prefill && env_int("RA_MIXED_OVERLAP", 1) != 0;
     if (has_decode) {
-        err = decode_workgroups(p, plan, dw.whole ? dw.nd : 0, &dw.nwg);
+        int fill = 0, cus = 0;
+        err = decode_workgroups(p, plan, dw.whole ? dw.nd : 0, &dw.nwg, &fill, &cus);
         if (err != hipSuccess) return err;
         if (overlap) {
             const int per_mille = env_int("RA_MIXED_DECODE_SHARE", plan.decode_share_pm);
             dw.nwg = std::max(1, std::min(dw.nwg, (int)((long long)dw.nwg * per_mille / 1000)));
+            if (env_int("RA_MIXED_ROUNDS", 1) != 0)
+                dw.nwg = whole_prefill_rounds(dw.nwg, fill, cus, plan.n_prefill_items);
         }
     }
     int4 *pre = (int4 *)(w + plan.off_prefill);

@@ -230,8 +230,10 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
 // (blocks: 16-row page blocks of all nd decode requests).
 int decode_heads_per_group(int D, int Hkv, long long blocks, int nd);
 // Decode workgroups per head group to launch on the current device (whole:
-// list entries when each workgroup takes whole requests, else 0).
-hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *nwg);
+// list entries when each workgroup takes whole requests, else 0); fill (if
+// not null) receives the count that puts one on every compute unit's
+// resident slots, cus (if not null) the device's compute units.
+hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *nwg, int *fill, int *cus);
 // Launches the decode kernel, records event 3, launches the merge kernel.
 hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream,
                          const StageEvents &ev);
