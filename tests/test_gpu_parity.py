@@ -227,29 +227,29 @@ def test_self_planned_prefill_matches_plan_kernel(D, monkeypatch):
     assert_close(out_self, ref, "self_plan_pre")
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_longest_first_items_over_64_requests(causal, monkeypatch):
-    """200 requests (several per lane of the in-kernel planner): chunks of
-    2-90 tokens after 0-600 tokens of context, with decode and empty requests
-    among them.  The prefill items go out longest first; the plan kernel's
+@pytest.mark.parametrize("n_req,causal", [(200, True), (200, False), (64, True), (65, True)])
+def test_longest_first_items_over_64_requests(n_req, causal, monkeypatch):
+    """n_req requests (200: several per lane of the in-kernel planner; 64 and
+    65 on both sides of its one-slot path): chunks of 2-90 tokens after 0-600
+    tokens of context, with decode and empty requests among them.  The prefill items go out longest first; the plan kernel's
     items (request order, RA_SELF_PLAN=0) give the same bits.  The decode
     requests are short, which would give self-planned workgroups whole
     requests (another split, so other rounding): RA_DECODE_WHOLE=0 keeps the
     plan kernel's equal page ranges in both runs."""
     monkeypatch.setenv("RA_DECODE_WHOLE", "0")
-    g = np.random.default_rng(83 + causal)
-    q = [int(x) for x in g.integers(0, 91, 200)]
+    g = np.random.default_rng(83 + causal + n_req)
+    q = [int(x) for x in g.integers(0, 91, n_req)]
     q = [1 if x % 17 == 3 else x for x in q]
-    c = [int(x) for x in g.integers(0, 601, 200)]
-    b = build_batch(q, c, num_q_heads=8, num_kv_heads=2, head_dim=128, causal=causal, seed=83 + causal,
-                    name="longest_first_200")
+    c = [int(x) for x in g.integers(0, 601, n_req)]
+    b = build_batch(q, c, num_q_heads=8, num_kv_heads=2, head_dim=128, causal=causal,
+                    seed=83 + causal + n_req, name=f"longest_first_{n_req}")
     out_self, kc_self, _ = run_gpu(b)
     monkeypatch.setenv("RA_SELF_PLAN", "0")
     out_plan, kc_plan, _ = run_gpu(b)
     assert torch.equal(out_self.view(torch.int16), out_plan.view(torch.int16))
     assert torch.equal(kc_self.view(torch.int16), kc_plan.view(torch.int16))
     ref, _, _ = oracle_full(b)
-    assert_close(out_self, ref, "longest_first_200")
+    assert_close(out_self, ref, f"longest_first_{n_req}")
 
 
 def test_more_decode_requests_than_a_grid_dimension():
