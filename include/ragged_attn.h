@@ -37,7 +37,8 @@
  *   out          [T][Hq][D]             bf16, device, written
  *
  * Supported: D in {64, 128, 256}; S a multiple of 16, at most 1024 (the kernels
- * walk the cache in 16-row blocks of a page); Hq % Hkv == 0; Hq / Hkv <= 16.
+ * walk the cache in 16-row blocks of a page); Hq % Hkv == 0; Hq / Hkv <= 16;
+ * L_r < 2^30 (key positions are 32-bit inside the kernels).
  *
  * Ownership and concurrency: the caller owns every buffer, the workspace
  * included; the library allocates no device memory and keeps no data

@@ -64,6 +64,9 @@ ra_status check_host_lens(const ra_shape *s, const int32_t *cu, const int32_t *c
         const long long L = (long long)ctx[r] + (cu[r + 1] - cu[r]);
         if (L > (long long)s->max_pages_per_req * s->page_size)
             return fail(RA_E_METADATA, "request %d: length %lld exceeds max_pages_per_req * S", r, L);
+        // The kernels index key positions (and tiles past them) in 32 bits.
+        if (L >= (1LL << 30))
+            return fail(RA_E_UNSUPPORTED, "request %d: length %lld of 2^30 tokens or more", r, L);
     }
     if (cu[R] != s->total_tokens)
         return fail(RA_E_METADATA, "cu_q_lens[R] = %d but total_tokens = %d", cu[R], s->total_tokens);

@@ -145,8 +145,10 @@ def test_forward_rejects_before_touching_the_gpu(lib):
     assert _forward_status(lib, shape_for(b), cu, ctx, variant=7) == 2
     bad = cu.clone(); bad[2] = 0
     assert _forward_status(lib, shape_for(b), bad, ctx) == 4
-    assert _forward_status(lib, shape_for(b, softmax_scale=-1.0) if False else
-                           shape_for(b, scale=float("inf")), cu, ctx) == 2
+    assert _forward_status(lib, shape_for(b, scale=-1.0), cu, ctx) == 2
+    assert _forward_status(lib, shape_for(b, scale=float("inf")), cu, ctx) == 2
+    huge = ctx.clone(); huge[0] = 1 << 30  # key positions are 32-bit inside the kernels
+    assert _forward_status(lib, shape_for(b, max_pages_per_req=1 << 27), cu, huge) == 3
 
 
 def test_empty_batch_is_a_no_op(lib):
