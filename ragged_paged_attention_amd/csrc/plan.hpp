@@ -62,13 +62,16 @@ __device__ __forceinline__ int wave_reduce_i(int x) {
 // ... (one round trip of loads); a binary search over the tile count, each
 // step a wave sum of per-request counts in closed form, finds the tile count
 // of item k, and a wave scan finds its request, whose metadata the owning
-// lane already holds.  q_tile must be a power of two.  A result that falls
-// outside the batch (not expected) turns the item into a no-op (it.x = -1).
+// lane already holds.  A result that falls outside the batch (not expected)
+// turns the item into a no-op (it.x = -1).
 template <int KR>
 __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k, int q_tile, int key_tile,
                                                          int4 &it, int4 &it2) {
     const int lane = threadIdx.x & 63, R = p.R, Hkv = p.Hkv;
+    // Query tiles: a shift when q_tile is a power of two (G a power of two).
+    const bool pow2 = (q_tile & (q_tile - 1)) == 0;
     const int qsh = __builtin_ctz(q_tile);
+    auto tiles_of = [&](int x) { return pow2 ? (x + q_tile - 1) >> qsh : (x + q_tile - 1) / q_tile; };
     int t0s[KR], q[KR], c[KR], nt[KR];
     int tmax = 0;
 #pragma unroll
@@ -78,7 +81,7 @@ __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k,
         const int qr = r < R ? p.cu_q_lens[r + 1] - t0s[j] : 0;
         q[j] = qr > 1 ? qr : 0;  // decode and empty requests have no prefill items
         c[j] = r < R ? p.context_lens[r] : 0;
-        nt[j] = (q[j] + q_tile - 1) >> qsh;
+        nt[j] = tiles_of(q[j]);
         if (q[j]) tmax = max(tmax, (c[j] + q[j] + key_tile - 1) / key_tile);
     }
     tmax = wave_reduce_i<true>(tmax);
@@ -90,7 +93,7 @@ __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k,
         if (q[j] == 0 || c[j] + q[j] < x) return 0;
         const int a = x - c[j];
         if (!p.causal || a <= 0) return nt[j];
-        return 1 + max(0, min(nt[j] - 1, nt[j] - ((a + q_tile - 1) >> qsh)));
+        return 1 + max(0, min(nt[j] - 1, nt[j] - tiles_of(a)));
     };
     // Items that read at least lam key tiles.
     auto at_least = [&](int lam) {
@@ -149,7 +152,7 @@ __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k,
     const int r = 64 * j + ln;
     const int t0 = __builtin_amdgcn_readlane(t0v, ln), qr = __builtin_amdgcn_readlane(qv, ln);
     const int ctx = __builtin_amdgcn_readlane(cv, ln);
-    const int ntiles = (qr + q_tile - 1) >> qsh;
+    const int ntiles = tiles_of(qr);
     if (j < 0 || r >= R || local < 0 || m < 0 || qr <= 1 || rank >= ntiles) {
         it = make_int4(-1, 0, 0, 0);
         it2 = make_int4(0, 0, 0, 0);

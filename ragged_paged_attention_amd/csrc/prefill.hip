@@ -3,10 +3,11 @@
 // head_dim 64, 128 and 256).
 //
 // Work unit: one workgroup of 8 wavefronts per (request r, kv head hk, query
-// tile of 256/G tokens), read from the plan kernel's item list or, for
-// batches of at most kSelfPlanReqs requests, found by the workgroup itself
-// (self_plan_prefill_item).  Its 256 query rows are the G query heads of the
-// group times the tile's tokens, so one K/V tile in LDS serves every head
+// tile of QT = floor(256/G) tokens), read from the plan kernel's item list
+// or, for batches of at most kSelfPlanReqs requests, found by the workgroup
+// itself (self_plan_prefill_item).  Its 256 query rows are the G query heads
+// of the group times the tile's tokens (row R: head R / QT, token R % QT; the
+// last 256 - G QT rows are idle), so one K/V tile in LDS serves every head
 // that reads it (grouped-query attention); wavefront w owns rows 32 w ..
 // 32 w + 31.
 //
@@ -235,9 +236,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 
     // This lane's query row R = 32 w + n32: head g = R / QT, token i = R % QT.
     const int R = 32 * w + n32;
+    // When G does not divide 256 the last 256 % G rows belong to no head.
     const int gh = R / QT;
     const int iq = R - gh * QT;
-    const bool rvalid = iq < tile_q;
+    const bool rvalid = iq < tile_q && gh < G;
     const int qi = q0 + (rvalid ? iq : 0);
     const int lim = rvalid ? (p.causal ? c + qi : L - 1) : -1;  // last visible key
     short8_t qb[KS];
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
     auto qoff = [&](int ks) { return (int)opaque((uint32_t)qoff0) ^ (16 * (ks - KQR)); };
     {
         // Q^T as the B operand: lane holds q[t0 + qi][hk*G + g][16ks + 8h2 .. +8].
-        const bf16_t *qrow = p.q + ((size_t)(t0 + qi) * Hq + hk * G + gh) * D + 8 * h2;
+        const bf16_t *qrow = p.q + ((size_t)(t0 + qi) * Hq + hk * G + min(gh, G - 1)) * D + 8 * h2;
         const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -632,9 +634,7 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
 
 }  // namespace
 
-bool prefill_supports(int D, int G) {
-    return (D == 64 || D == 128 || D == 256) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
-}
+bool prefill_supports(int D, int G) { return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16; }
 
 int prefill_rows(int D) {
     switch (D) {

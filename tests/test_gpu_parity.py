@@ -94,10 +94,14 @@ SMALL = [
     (6, 5, 50, 60, 8, 8, 128, 0.5, True),      # G = 1
     (7, 5, 50, 60, 16, 1, 64, 0.5, True),      # G = 16
     (8, 4, 45, 80, 8, 1, 128, 0.5, True),      # G = 8
-    (9, 5, 60, 100, 12, 4, 128, 0.5, True),    # G = 3: generic fallback
+    (9, 5, 60, 100, 12, 4, 128, 0.5, True),    # G = 3 (256 rows: 85 tokens, one idle row)
     (10, 5, 60, 100, 32, 8, 128, 0.3, False),  # non-causal
     (11, 3, 20, 3000, 16, 4, 128, 0.7, True),  # long contexts
     (12, 6, 90, 50, 4, 2, 256, 0.4, False),
+    (13, 5, 130, 200, 40, 8, 128, 0.4, True),  # G = 5 (51 tokens per tile, one idle row)
+    (14, 5, 130, 200, 28, 4, 128, 0.4, True),  # G = 7 (36 tokens, four idle rows)
+    (15, 4, 110, 150, 12, 2, 64, 0.4, False),  # G = 6, non-causal (42 tokens, four idle rows)
+    (16, 4, 90, 150, 24, 2, 256, 0.4, True),   # G = 12 at D=256 (21 tokens, four idle rows)
 ]
 
 
