@@ -251,6 +251,9 @@ hipError_t side_stream(SideStream **out) {
 // workload, 96 decode requests and 512 prefill items: 0.53 of the units,
 // 4.2 rounds, 442 us per call; 0.5 and 0.6, 4 and 5 rounds, 430 us.)
 int whole_prefill_rounds(int nwg, int fill, int cus, int items) {
+    // (The caller caps the result at its full decode grid: with little decode
+    // work that grid is far below fill, and a split sized in compute units
+    // would ask for more workgroups than the batch has pages.)
     if (fill <= 0 || cus <= 0 || items <= 0 || nwg >= fill) return nwg;
     const double dec = (double)cus * nwg / fill;  // units the decode kernel holds
     const int free_units = cus - (int)dec;
@@ -292,11 +295,17 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
     dw.hw = plan.decode_hw;
-    // Batches of at most kSelfPlanReqs requests skip the plan kernel: the
-    // decode and prefill kernels find their own work, and the decode list is
-    // then every request of the batch.
-    const bool self_plan = p.R <= kSelfPlanReqs && env_int("RA_SELF_PLAN", 1) != 0;
+    // Small batches skip the plan kernel: the decode and prefill kernels find
+    // their own work, and the decode list is then every request of the batch.
+    // Every prefill workgroup repeats its search over all requests, which pays
+    // only with one request per lane (at most kSelfPlanPrefillReqs); a batch
+    // with prefill chunks and more requests runs the plan kernel (measured,
+    // 512 requests x 64 tokens: 354 us planning in every workgroup, 259 us
+    // with the plan kernel's list).  Decode-only batches plan in the kernel up
+    // to kSelfPlanReqs requests (one search per decode workgroup).
     const bool has_decode = plan.n_decode_reqs > 0, has_prefill = plan.n_prefill_items > 0;
+    const bool self_plan = p.R <= (has_prefill ? kSelfPlanPrefillReqs : kSelfPlanReqs) &&
+                           env_int("RA_SELF_PLAN", 1) != 0;
     dw.self_plan = self_plan ? 1 : 0;
     if (self_plan && has_decode) dw.nd = p.R;
     // Short contexts (at most 40 16-row blocks per decode request on
@@ -317,11 +326,17 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         err = decode_workgroups(p, plan, dw.whole ? dw.nd : 0, &dw.nwg, &fill, &cus);
         if (err != hipSuccess) return err;
         if (overlap) {
+            // The reduced grid never exceeds the one computed above, which
+            // respects the pages per workgroup and the workspace's slots.
+            const int full = dw.nwg;
             const int per_mille = env_int("RA_MIXED_DECODE_SHARE", plan.decode_share_pm);
-            dw.nwg = std::max(1, std::min(dw.nwg, (int)((long long)dw.nwg * per_mille / 1000)));
+            dw.nwg = std::max(1, std::min(full, (int)((long long)full * per_mille / 1000)));
             if (env_int("RA_MIXED_ROUNDS", 1) != 0)
-                dw.nwg = whole_prefill_rounds(dw.nwg, fill, cus, plan.n_prefill_items);
+                dw.nwg = std::min(full, whole_prefill_rounds(dw.nwg, fill, cus, plan.n_prefill_items));
         }
+        // The workspace holds partial slots for decode_wg_cap workgroups per
+        // head group.
+        if (dw.nwg > plan.decode_wg_cap) return hipErrorInvalidValue;
     }
     int4 *pre = (int4 *)(w + plan.off_prefill);
     err = ev.record(0);

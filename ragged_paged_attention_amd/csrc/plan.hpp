@@ -16,8 +16,9 @@
 // Self-planned batches hand the items out longest first across requests
 // (self_plan_prefill_item); the plan kernel writes them request by request.
 //
-// The host computes counts and the workspace layout only.  Batches of at
-// most kSelfPlanReqs requests need no further planning: the decode and
+// The host computes counts and the workspace layout only.  Decode-only
+// batches of at most kSelfPlanReqs requests, and batches with prefill chunks
+// of at most kSelfPlanPrefillReqs, need no further planning: the decode and
 // prefill kernels find their own work from the device metadata.  Larger
 // batches run a one-workgroup plan kernel that writes the decode request
 // list, the workgroup start table and the prefill items from the device
@@ -37,6 +38,9 @@ namespace ra {
 // Largest batch whose decode and prefill kernels find their own work with a
 // wave scan over the requests; larger batches run the plan kernel.
 constexpr int kSelfPlanReqs = 512;
+// Largest batch with prefill chunks that plans inside the kernels (one
+// request per lane of the prefill kernel's search).
+constexpr int kSelfPlanPrefillReqs = 64;
 
 // Sum (or max) over the wavefront, the same in every lane: DPP within each
 // row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
@@ -162,12 +166,11 @@ __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k,
     it2 = make_int4(ctx, qr, 0, 0);
 }
 
-// As above for any batch of at most kSelfPlanReqs requests (one slot per
-// lane when there are at most 64).
+// As above for a batch of at most kSelfPlanPrefillReqs requests.
 __device__ __forceinline__ void self_plan_prefill_item(const Params &p, int k, int q_tile, int key_tile,
                                                        int4 &it, int4 &it2) {
-    if (p.R <= 64) self_plan_prefill_item_k<1>(p, k, q_tile, key_tile, it, it2);
-    else self_plan_prefill_item_k<kSelfPlanReqs / 64>(p, k, q_tile, key_tile, it, it2);
+    static_assert(kSelfPlanPrefillReqs == 64, "one request per lane");
+    self_plan_prefill_item_k<1>(p, k, q_tile, key_tile, it, it2);
 }
 
 // Upper bound of decode workgroups per call (all head groups together); it

@@ -4,7 +4,7 @@
 //
 // Work unit: one workgroup of 8 wavefronts per (request r, kv head hk, query
 // tile of QT = floor(256/G) tokens), read from the plan kernel's item list
-// or, for batches of at most kSelfPlanReqs requests, found by the workgroup
+// or, for batches of at most kSelfPlanPrefillReqs requests, found by the workgroup
 // itself (self_plan_prefill_item).  Its 256 query rows are the G query heads
 // of the group times the tile's tokens (row R: head R / QT, token R % QT; the
 // last 256 - G QT rows are idle), so one K/V tile in LDS serves every head

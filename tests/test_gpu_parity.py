@@ -163,9 +163,13 @@ EDGES = {
     # with prefill chunks and empty requests in the batch
     "short_whole_requests": ([1] * 70, [(17 * i) % 90 for i in range(70)], 32, 8, 128),
     "short_whole_mixed": ([1, 1, 5, 1, 0, 1, 1, 33, 1, 1] * 6, [(23 * i) % 70 for i in range(60)], 16, 8, 256),
-    # prefill-only batches likewise find their items in the prefill kernel
+    # batches with prefill chunks find their items in the prefill kernel up
+    # to 64 requests; past that the plan kernel writes them
+    "prefill_only_64": ([2 + (i % 5) for i in range(64)], [(13 * i) % 40 for i in range(64)], 8, 2, 64),
+    "prefill_only_65": ([2 + (i % 5) for i in range(65)], [(13 * i) % 40 for i in range(65)], 8, 2, 64),
     "prefill_only_512": ([2 + (i % 5) for i in range(512)], [(13 * i) % 40 for i in range(512)], 8, 2, 64),
-    "prefill_only_513": ([2 + (i % 5) for i in range(513)], [(13 * i) % 40 for i in range(513)], 8, 2, 64),
+    "mixed_64": ([1 if i % 3 else 9 for i in range(64)], [(19 * i) % 200 for i in range(64)], 16, 4, 128),
+    "mixed_65": ([1 if i % 3 else 9 for i in range(65)], [(19 * i) % 200 for i in range(65)], 16, 4, 128),
     "prefill_and_empty": ([0, 3, 0, 70, 2, 0], [5, 7, 0, 40, 300, 9], 32, 8, 128),
     # more requests than the plan kernel keeps in LDS (its searches then run
     # over global memory), decode and prefill mixed
@@ -231,15 +235,15 @@ def test_self_planned_prefill_matches_plan_kernel(D, monkeypatch):
     assert_close(out_self, ref, "self_plan_pre")
 
 
-@pytest.mark.parametrize("n_req,causal", [(200, True), (200, False), (64, True), (65, True)])
-def test_longest_first_items_over_64_requests(n_req, causal, monkeypatch):
-    """n_req requests (200: several per lane of the in-kernel planner; 64 and
-    65 on both sides of its one-slot path): chunks of 2-90 tokens after 0-600
-    tokens of context, with decode and empty requests among them.  The prefill items go out longest first; the plan kernel's
-    items (request order, RA_SELF_PLAN=0) give the same bits.  The decode
-    requests are short, which would give self-planned workgroups whole
-    requests (another split, so other rounding): RA_DECODE_WHOLE=0 keeps the
-    plan kernel's equal page ranges in both runs."""
+@pytest.mark.parametrize("n_req,causal", [(64, True), (64, False), (40, True), (200, True)])
+def test_longest_first_items(n_req, causal, monkeypatch):
+    """n_req requests (up to 64: the prefill kernel finds its items, longest
+    first; 200: the plan kernel writes them in request order in both runs):
+    chunks of 2-90 tokens after 0-600 tokens of context, with decode and empty
+    requests among them.  The plan kernel's items (RA_SELF_PLAN=0) give the
+    same bits.  The decode requests are short, which would give self-planned
+    workgroups whole requests (another split, so other rounding):
+    RA_DECODE_WHOLE=0 keeps the plan kernel's equal page ranges in both runs."""
     monkeypatch.setenv("RA_DECODE_WHOLE", "0")
     g = np.random.default_rng(83 + causal + n_req)
     q = [int(x) for x in g.integers(0, 91, n_req)]
@@ -254,6 +258,23 @@ def test_longest_first_items_over_64_requests(n_req, causal, monkeypatch):
     assert torch.equal(kc_self.view(torch.int16), kc_plan.view(torch.int16))
     ref, _, _ = oracle_full(b)
     assert_close(out_self, ref, f"longest_first_{n_req}")
+
+
+def test_small_decode_part_beside_many_prefill_items(monkeypatch):
+    """A mixed batch whose decode part is four short requests (76 pages) and
+    whose prefill part is 58 chunks, with equal page ranges forced for the
+    decode kernel (RA_DECODE_WHOLE=0): the decode grid launched beside the
+    prefill kernel stays within the page-limited grid and the workspace's
+    partial slots (a split sized in compute units once asked for hundreds of
+    workgroups here, and the decode rows were never written)."""
+    monkeypatch.setenv("RA_DECODE_WHOLE", "0")
+    g = np.random.default_rng(147)
+    q = [int(x) for x in g.integers(0, 91, 64)]
+    q = [1 if x % 17 == 3 else x for x in q]
+    c = [int(x) for x in g.integers(0, 601, 64)]
+    b = build_batch(q, c, num_q_heads=8, num_kv_heads=2, head_dim=128, causal=False, seed=147,
+                    name="small_decode_many_prefill")
+    check_small(b, "specialised")
 
 
 def test_more_decode_requests_than_a_grid_dimension():
