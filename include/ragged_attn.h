@@ -151,8 +151,9 @@ ra_status ra_forward_variant(const ra_shape *shape,
  * the plan kernel, the prefill kernel, the decode kernel and the decode
  * merge kernel, in that order (a kernel that does not run still has its
  * event recorded, so its duration reads as ~0 -- the plan kernel runs only
- * for batches of more than 512 requests; the generic variant runs as the
- * prefill kernel).  n_events must be 5; events are not created,
+ * for decode-only batches of more than 512 requests and batches with
+ * prefill chunks of more than 64; the generic variant runs as the prefill
+ * kernel).  n_events must be 5; events are not created,
  * synchronised or destroyed by the library.
  */
 ra_status ra_forward_profiled(const ra_shape *shape,
