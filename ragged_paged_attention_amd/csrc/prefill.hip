@@ -407,8 +407,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
         }
         l_run += lsum;
     };
-    // O += V . P over one tile alone.
-    auto pv_only = [&](auto sv) {
+    // O += V . P over one tile alone (P^T given as bf16 B operands).
+    auto pv_with = [&](auto sv, const short8_t (&pp)[N / 16]) {
         const bf16_t *Vs = vst(sv);
 #pragma unroll
         for (int s16 = 0; s16 < N / 16; ++s16)
@@ -418,8 +418,40 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
                 const short4_t lo = lds_read_tr16(v);
                 const short4_t hi = lds_read_tr16(v + 8 * D);
                 const short8_t va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s16], o[md], 0, 0, 0);
+                o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pp[s16], o[md], 0, 0, 0);
             }
+    };
+    auto pv_only = [&](auto sv) { pv_with(sv, pb); };
+    // Exponentials of a masked tile (one that crosses some row's last key,
+    // where the rows that see the fewest keys live) as a bf16 hi + lo pair:
+    // hi goes to pb for the PV product of the next phase, and O += V . lo
+    // right here, so the weights keep ~16 bits.  With one bf16 P, a row
+    // that sees a handful of keys has weights of order one, and their
+    // relative rounding (2^-9 each) plus the output's own rounding can
+    // exceed 1e-2 on values of a few units.  The rescale that follows the
+    // next row max applies to both halves alike.
+    auto exp_lo_pv = [&](const float16_t (&s)[KB], auto sv) {
+        const float nref = -m_run;
+        float lsum = 0.f;
+        short8_t plo[N / 16];
+#pragma unroll
+        for (int s16 = 0; s16 < N / 16; ++s16) {
+            uint32_t w4[4], l4[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int e = 8 * s16 + 2 * e2;
+                const float a = fast_exp2(fmaf(s[e / 16][e % 16], sl2, nref));
+                const float b = fast_exp2(fmaf(s[(e + 1) / 16][(e + 1) % 16], sl2, nref));
+                w4[e2] = cvt_pk_bf16(a, b);
+                l4[e2] = cvt_pk_bf16(a - bf16_lo(w4[e2]), b - bf16_hi(w4[e2]));
+                lsum = pair_sum_bf16(w4[e2], lsum);
+                lsum = pair_sum_bf16(l4[e2], lsum);
+            }
+            pb[s16] = __builtin_bit_cast(short8_t, w4);
+            plo[s16] = __builtin_bit_cast(short8_t, l4);
+        }
+        l_run += lsum;
+        pv_with(sv, plo);
     };
     // Row max of S(t) alone, masking keys past each row's last one if MASKED.
     auto max_only = [&](auto masked, int t, float16_t (&s)[KB]) {
@@ -520,10 +552,16 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
         float16_t(&sn)[KB] = sbuf[u & 1];
         float16_t(&so)[KB] = sbuf[(u + 1) & 1];
         const bool has_exp = t >= 1 && t <= ntw, has_qk = t < ntw;
-        if (has_exp && has_qk) {
+        // A masked tile t-1 takes the hi + lo path (its V is still in LDS:
+        // stage (t-1) % 4 is reloaded only at B(t+1)), without interleaving.
+        const bool lo = has_exp && masked_tile(t - 1);
+        if (has_exp && has_qk && !lo) {
             a_full(ic<u>(), sn, so);
         } else {
-            if (has_exp) exp_only(so);
+            if (has_exp) {
+                if (lo) exp_lo_pv(so, ic<(u + 3) & 3>());
+                else exp_only(so);
+            }
             if (has_qk) qk_only(ic<u>(), sn);
         }
     };

@@ -3,9 +3,8 @@
 Bar: KV caches bit-exact over the whole tensors; attention output within
 max-abs 1e-2 of the oracle (bf16 I/O, fp32 accumulation); no NaN anywhere
 (unused cache slots hold the bf16 NaN sentinel, so a stray read shows up).
-Small batches are compared in full; the full-size workloads are compared on
-sampled (token, head) rows the oracle evaluates one by one, plus the full
-caches.
+Small batches and the full-size workloads are compared in full; one very long
+prefill chunk is compared on a dense systematic sample of its rows.
 """
 from __future__ import annotations
 
@@ -57,15 +56,35 @@ def oracle_full(b: Batch):
                           b.slot_mapping.numpy(), scale=b.effective_scale(), causal=b.causal)
 
 
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |x| (8 significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+def bound(ref: np.ndarray) -> np.ndarray:
+    """Per-element bound: 1e-2, except where the bf16 grid itself is coarser.
+
+    For |o| >= 4 half a bf16 ulp is 1/64 > 1e-2, so even the correctly
+    rounded output can lie up to 0.0156 from the fp64 value; there an
+    element must be within half an ulp plus 1e-3 (the fp32 pipeline's own
+    error) of the oracle.  Below 4 the bound is exactly 1e-2."""
+    return np.maximum(TOL, bf16_half_ulp(ref) + 1e-3)
+
+
 def assert_close(out: torch.Tensor, ref: np.ndarray, what=""):
     o = out.float().numpy()
     assert not np.isnan(o).any(), f"{what}: NaN in output"
     err = np.abs(o - ref)
     worst = float(err.max(initial=0.0))
-    if worst > TOL:
-        idx = np.unravel_index(int(np.argmax(err)), err.shape)
-        raise AssertionError(f"{what}: max abs error {worst:.3g} > {TOL} at (token, head, dim) {idx}: "
-                             f"GPU {o[idx]:.6g}, oracle {ref[idx]:.6g}")
+    if err.size and not (err <= bound(ref)).all():
+        idx = np.unravel_index(int(np.argmax(err - bound(ref))), err.shape)
+        raise AssertionError(f"{what}: abs error {err[idx]:.3g} > {bound(ref)[idx]:.3g} at (token, head, dim) "
+                             f"{idx}: GPU {o[idx]:.6g}, oracle {ref[idx]:.6g} (max abs error {worst:.3g})")
+    over = int((err > TOL).sum())
+    if over:
+        say(f"[parity] {what}: {over} of {err.size} elements beyond 1e-2, all at |o| >= 4 within half a "
+            f"bf16 ulp + 1e-3 of the oracle (max abs error {worst:.3g})")
     return worst
 
 
@@ -112,6 +131,43 @@ def test_random_batches(case, variant):
     b = random_batch(seed, num_reqs=R, max_q=mq, max_ctx=mc, num_q_heads=Hq, num_kv_heads=Hkv,
                      head_dim=D, decode_frac=frac, causal=causal)
     check_small(b, variant)
+
+
+# Unit-normal batches of prefill chunks without prior context, found by a CPU
+# search (a model of the rounding of a one-bf16 P in the PV product, checked
+# against the oracle) over random batches in the space of the suite's random
+# cases.  With one bf16 P, rows that see only a few keys have weights of order
+# one, and the relative rounding of each weight plus the output's own
+# rounding put one element 1.01-1.09 x 1e-2 from the oracle where |o| lies in
+# [2, 4); with the hi + lo P of masked tiles the error is the output's
+# rounding alone.  The last four have an element at |o| >= 4 whose correctly
+# rounded bf16 value is itself 0.0122-0.0148 from the fp64 result: no bf16
+# output can meet 1e-2 there, and those elements are held to half an ulp +
+# 1e-3 (assert_close).
+FEW_KEY_SEEDS = [
+    # (seed, R, max_q, max_ctx, Hq, Hkv, D, decode_frac, causal)
+    (243971, 2, 12, 0, 80, 8, 256, 0.3, True),
+    (189135, 4, 95, 0, 96, 8, 256, 0.0, True),
+    (554516, 5, 112, 0, 48, 8, 128, 0.0, True),
+    (75510, 4, 49, 0, 30, 2, 128, 0.0, True),
+    (921097, 3, 43, 0, 4, 1, 64, 0.3, True),
+    (721805, 3, 98, 0, 36, 4, 128, 0.3, True),
+    (513117, 2, 67, 0, 120, 8, 128, 0.0, True),
+    (99883, 1, 114, 0, 112, 8, 128, 0.3, True),
+    (921102, 3, 70, 0, 104, 8, 256, 0.0, False),
+    (896824, 2, 84, 0, 12, 2, 128, 0.3, True),
+    (367049, 4, 21, 0, 12, 2, 64, 0.0, True),
+    (308641, 6, 26, 0, 96, 8, 256, 0.3, True),
+    (859117, 4, 71, 0, 32, 4, 64, 0.3, True),
+]
+
+
+@pytest.mark.parametrize("case", FEW_KEY_SEEDS, ids=lambda c: f"seed{c[0]}")
+def test_few_key_prefill_rows(case):
+    seed, R, mq, mc, Hq, Hkv, D, frac, causal = case
+    b = random_batch(seed, num_reqs=R, max_q=mq, max_ctx=mc, num_q_heads=Hq, num_kv_heads=Hkv,
+                     head_dim=D, decode_frac=frac, causal=causal)
+    check_small(b, "specialised")
 
 
 PAGED = [
@@ -346,35 +402,17 @@ def test_graph_capture_replays_match_eager(n_decode):
     assert_close(want.cpu(), ref, f"graph_{n_decode}")
 
 
-def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
-    """Half a bf16 ulp at |x| (8 significant bits)."""
-    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
-    return 2.0 ** (e - 8)
-
-
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("scale,D", [(0.3, 128), (0.02, 64), (0.125, 256), (1.0, 128)])
 def test_explicit_softmax_scale(scale, D, variant):
     """A softmax scale other than 1/sqrt(D), on decode requests and prefill
     chunks with context, both variants.  At scale 1.0 (logits with a standard
     deviation of about 11) rows are nearly one-hot on values up to |v| ~ 4.5,
-    where half a bf16 ulp (1/64) exceeds 1e-2: there an element passes if it
-    is within 1e-3 + half an ulp of the oracle (the output's own rounding),
-    and the test reports how many needed that."""
+    where half a bf16 ulp exceeds 1e-2 (the per-element bound of
+    assert_close)."""
     b = build_batch([1, 70, 1, 33], [900, 150, 20, 0], num_q_heads=16, num_kv_heads=4, head_dim=D,
                     scale=scale, seed=int(1000 * scale) + D, name=f"scale_{scale}_{D}")
-    if scale < 1.0:
-        check_small(b, variant)
-        return
-    out, kc, vc = run_gpu(b, variant)
-    ref, rkc, rvc = oracle_full(b)
-    assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc)
-    o = out.float().numpy()
-    err = np.abs(o - ref)
-    bound = np.maximum(TOL, 1e-3 + bf16_half_ulp(ref))
-    assert not np.isnan(o).any() and (err <= bound).all(), f"max abs error {err.max():.3g}"
-    say(f"[parity] scale 1.0: {int((err > TOL).sum())} of {err.size} elements beyond 1e-2, "
-        f"all within 1e-3 + half a bf16 ulp (max error {err.max():.3g})")
+    check_small(b, variant)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -395,23 +433,10 @@ def test_fresh_decode_returns_v_new():
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads: whole caches bit-exact, sampled rows against the oracle.
+# Full-size workloads: whole caches bit-exact and every output element against
+# the oracle.  The one 16384-token chunk (3.3 TFLOP of fp64 oracle work when
+# causal) is compared on a dense systematic sample instead.
 # ---------------------------------------------------------------------------
-def sample_rows(b: Batch, n, seed):
-    rng = np.random.default_rng(seed)
-    T, Hq = b.total_tokens, b.num_q_heads
-    cu = b.cu_q_lens.numpy()
-    toks = set()
-    for r in range(b.num_reqs):  # first and last token of every request
-        if cu[r + 1] > cu[r]:
-            toks.update([int(cu[r]), int(cu[r + 1] - 1)])
-    toks = sorted(toks)
-    extra = rng.integers(0, T, size=max(0, n - len(toks)))
-    tokens = np.array(list(toks) + list(extra), dtype=np.int32)
-    heads = rng.integers(0, Hq, size=len(tokens)).astype(np.int32)
-    return tokens, heads
-
-
 FULL = ("decode", "mixed", "prefill", "prefill_noncausal", "decode_d256", "prefill_d256")
 
 
@@ -428,23 +453,18 @@ def test_full_workload(name):
     assert np.array_equal(u16(kc), rkc), "k_cache differs from the oracle's scatter"
     assert np.array_equal(u16(vc), rvc), "v_cache differs from the oracle's scatter"
     del kc, vc
-    o = out.float().numpy()
-    assert not np.isnan(o).any(), "NaN in output"
-    tokens, heads = sample_rows(b, 384, seed=7)
-    ref = oracle.attention_rows(u16(b.q), rkc, rvc, b.page_table.numpy(), b.cu_q_lens.numpy(),
-                                b.context_lens.numpy(), tokens, heads,
-                                scale=b.effective_scale(), causal=b.causal)
-    got = o[tokens, heads, :]
-    worst = float(np.abs(got - ref).max())
-    say(f"[parity] full workload {name}: max abs error {worst:.3g} over {len(tokens)} rows")
-    assert worst <= TOL
+    ref = oracle.attention(u16(b.q), rkc, rvc, b.page_table.numpy(), b.cu_q_lens.numpy(),
+                           b.context_lens.numpy(), scale=b.effective_scale(), causal=b.causal)
+    worst = assert_close(out, ref, name)
+    say(f"[parity] full workload {name}: max abs error {worst:.3g} over all {ref.size} elements")
 
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_one_long_prefill_chunk(causal):
     """One 16384-token chunk after 4096 tokens of context (the longest key
-    loops the prefill kernel runs), sampled rows against the oracle and the
-    whole caches bit-exact."""
+    loops the prefill kernel runs): whole caches bit-exact; every q head of
+    every 16th token, plus the first and last 64 tokens, against the oracle
+    (about 1/14 of the output)."""
     b = build_batch([16384], [4096], num_q_heads=32, num_kv_heads=8, head_dim=128, causal=causal,
                     seed=84, name="long_chunk")
     out, kc, vc = run_gpu(b)
@@ -453,7 +473,10 @@ def test_one_long_prefill_chunk(causal):
     assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc)
     o = out.float().numpy()
     assert not np.isnan(o).any()
-    tokens, heads = sample_rows(b, 256, seed=9)
+    T, Hq = b.total_tokens, b.num_q_heads
+    toks = np.unique(np.concatenate([np.arange(0, T, 16), np.arange(64), np.arange(T - 64, T)]))
+    tokens = np.repeat(toks, Hq).astype(np.int32)
+    heads = np.tile(np.arange(Hq), len(toks)).astype(np.int32)
     ref = oracle.attention_rows(u16(b.q), rkc, rvc, b.page_table.numpy(), b.cu_q_lens.numpy(),
                                 b.context_lens.numpy(), tokens, heads, scale=b.effective_scale(),
                                 causal=b.causal)

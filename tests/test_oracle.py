@@ -179,6 +179,31 @@ def test_dominant_logit_selects_its_value():
     np.testing.assert_allclose(out[0, 0], V[5, 0], rtol=0, atol=1e-20 + 40 * math.exp(-64))
 
 
+@pytest.mark.parametrize("idx", [0, 1, 3, 7])
+def test_attention_rows_matches_dense_and_full(idx):
+    """oracle_attention_rows (the per-(token, head) entry the long-chunk GPU
+    test samples with) against the independent dense numpy formulation, and
+    bit for bit against the whole-batch oracle_attention: random (token, head)
+    pairs in random order, repeats included, every first and last token of a
+    request and every q head."""
+    b = small_batches()[idx]
+    out, kc, vc = run_oracle(b)
+    dense = dense_numpy(b)
+    rng = np.random.default_rng(40 + idx)
+    T, Hq = b.total_tokens, b.num_q_heads
+    cu = b.cu_q_lens.tolist()
+    edge = [t for r in range(b.num_reqs) if cu[r + 1] > cu[r] for t in (cu[r], cu[r + 1] - 1)]
+    tokens = np.concatenate([rng.integers(0, T, 3 * T), np.repeat(edge, Hq)]).astype(np.int32)
+    heads = np.concatenate([rng.integers(0, Hq, 3 * T), np.tile(np.arange(Hq), len(edge))]).astype(np.int32)
+    perm = rng.permutation(len(tokens))
+    tokens, heads = tokens[perm], heads[perm]
+    rows = oracle.attention_rows(u16(b.q), kc, vc, b.page_table.numpy(), b.cu_q_lens.numpy(),
+                                 b.context_lens.numpy(), tokens, heads, scale=b.effective_scale(),
+                                 causal=b.causal)
+    np.testing.assert_allclose(rows, dense[tokens, heads], rtol=0, atol=1e-12)
+    assert np.array_equal(rows, out[tokens, heads])
+
+
 # --------------------------------------------------------------------------
 # Invariants
 # --------------------------------------------------------------------------
@@ -373,6 +398,9 @@ MUTANTS = {
                        "long long page = p->page_table[(long long)r * p->max_pages + j % p->S];"),
     "q_head_stride": ("p->q + ((long long)t * p->Hq + h) * D",
                       "p->q + ((long long)t * p->Hq + h / G) * D"),
+    "rows_request_of_pair": ("attend_one(&p, req[tokens[i]], tokens[i], heads[i]",
+                             "attend_one(&p, req[i % T], tokens[i], heads[i]"),
+    "rows_head_of_pair": ("tokens[i], heads[i], scores", "tokens[i], heads[i] / 2, scores"),
 }
 
 
@@ -389,6 +417,15 @@ def _pins_pass(lib) -> bool:
         for t, slot in enumerate(b.slot_mapping.tolist()):
             if not (kc[slot // S, slot % S] == u16(b.k_new)[t]).all():
                 return False
+        # the per-(token, head) entry, on every pair in reverse order
+        T, Hq = b.total_tokens, b.num_q_heads
+        tokens = np.repeat(np.arange(T), Hq)[::-1].astype(np.int32)
+        heads = np.tile(np.arange(Hq), T)[::-1].astype(np.int32)
+        rows = oracle.attention_rows(u16(b.q), kc, vc, b.page_table.numpy(), b.cu_q_lens.numpy(),
+                                     b.context_lens.numpy(), tokens, heads,
+                                     scale=b.effective_scale(), causal=b.causal, lib=lib)
+        if not (np.max(np.abs(rows - ref[tokens, heads]), initial=0.0) < 1e-12):
+            return False
     return True
 
 
