@@ -8,12 +8,19 @@ decode batch (128 requests x 1 new token, contexts U[1024, 8192], Hq=32,
 Hkv=8, head_dim=128, page 16, bf16).  Prints ONE JSON line on stdout.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--variant V]
+                  [--extra-configs A,B,...|none]
 
 Roofline: the dominant kernel's algorithmic bytes (HBM-bound decode) or
 FLOPs (MFMA-bound prefill) per launch divided by its average launch time,
 measured with hipEvents the library records on its own stream around each
 stage.  The oracle (fp64 CPU) is timed on a bounded sample of the same
 workload as the CPU baseline.
+
+After the headline workload the same measurement runs for the other
+workloads (causal and non-causal prefill, the mixed batch, and the
+head_dim-256 decode and prefill batches), each under the line's "configs"
+key with its own roofline and a shorter CPU baseline; a mixed batch also
+reports max(B / 8 TB/s, F / bf16 peak) over its overlapped step time.
 """
 from __future__ import annotations
 
@@ -353,6 +360,11 @@ def main():
     ap.add_argument("--variant", default="auto", choices=list(binding.VARIANTS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-baseline budget (0 disables the oracle leg)")
+    ap.add_argument("--extra-configs", default="prefill,prefill_noncausal,mixed,decode_d256,prefill_d256",
+                    help="workloads timed after the headline one, under the line's 'configs' key "
+                         "(comma-separated; 'none' for the headline only)")
+    ap.add_argument("--extra-cpu-seconds", type=float, default=4.0,
+                    help="CPU-baseline budget of each extra workload")
     ap.add_argument("--sweep-decode", action="store_true",
                     help="instead of the contract line: one JSON line per decode context length "
                          "(128 requests x 1 token, context 128 .. 8192), HBM fraction against context")
@@ -386,15 +398,44 @@ def main():
         sweep_shapes(args)
         return
 
-    log(f"[bench] building inputs for {args.config}")
-    b = config(args.config)
+    extras = [] if args.extra_configs in ("", "none") else args.extra_configs.split(",")
+    for name in extras:
+        if name not in CONFIGS:
+            raise SystemExit(f"unknown config {name!r} in --extra-configs")
+    res = measure(args.config, args, cpu_budget=args.cpu_seconds, per_call=True)
+    line = {
+        "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+    }
+    line.update({k: v for k, v in res.items() if k not in line and k not in ("metric", "value", "unit")})
+    line["context"] = {"pages_decode_mbu_tpu7x": 0.86, "pages_prefill_mfu_tpu7x": 0.73,
+                       "pages_prefill_mfu_causal_tpu7x": 0.63}
+    if extras:
+        line["configs"] = {}
+        for name in extras:
+            if name == args.config:
+                continue
+            r = measure(name, args, cpu_budget=args.extra_cpu_seconds, per_call=False)
+            line["configs"][name] = r
+    print(json.dumps(line), flush=True)
+
+
+def measure(name: str, args, cpu_budget: float, per_call: bool) -> dict:
+    """Times one workload: --steps plain calls between events (the step), the
+    same number of calls with stage events (per-kernel times), and for the
+    headline also single calls and an L2/MALL-flushed pass; then the dominant
+    kernel's roofline and the oracle on a bounded sample."""
+    log(f"[bench] building inputs for {name}")
+    b = config(name)
     dev = torch.device("cuda:0")
     dt = [t.to(dev) for t in (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
                               b.cu_q_lens, b.context_lens, b.slot_mapping)]
     call = binding.Prepared(*dt, causal=b.causal, scale=b.scale or None, variant=args.variant,
                             cu_q_lens_host=b.cu_q_lens, context_lens_host=b.context_lens)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    log(f"[bench] R={b.num_reqs} T={b.total_tokens} pages={b.num_pages} "
+    log(f"[bench] {name}: R={b.num_reqs} T={b.total_tokens} pages={b.num_pages} "
         f"workspace={call.workspace.numel()} B; warmup {args.warmup}")
     for _ in range(args.warmup):
         call(stream)
@@ -413,7 +454,8 @@ def main():
 
     # Per-kernel durations: K more calls that record hipEvents at the kernel
     # boundaries on the same stream (the events cost a few us each, so these
-    # calls are not the ones `value` is timed on).
+    # calls are not the ones `value` is timed on; a mixed batch runs its
+    # kernels one after the other in them, so each is timed alone).
     timers = [binding.StageTimer() for _ in range(args.steps)]
     for k in range(args.steps):
         call(stream, timers[k])
@@ -421,7 +463,7 @@ def main():
     stages = {s: float(np.mean([t.stage_ms()[s] for t in timers])) for s in binding.STAGES}
     for t in timers:
         t.close()
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step; kernels (us): "
+    log(f"[bench] {name}: {ms_per_step * 1e3:.1f} us/step; kernels (us): "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
 
     # Distribution of single calls (an event pair around each call), and for
@@ -444,7 +486,7 @@ def main():
 
     single = per_call_us(args.steps)
     flushed = None
-    if stages["decode"] >= stages["prefill"]:
+    if per_call and stages["decode"] >= stages["prefill"]:
         junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         fl = per_call_us(args.steps, between=junk.zero_)
         del junk
@@ -468,7 +510,7 @@ def main():
         achieved = units / kern_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
-                "traffic": measured_traffic("decode", args.config) if dominant == "decode" else None,
+                "traffic": measured_traffic("decode", name) if dominant == "decode" else None,
                 "kernel": "decode_kernel" if args.variant != "generic" else "generic_kernel",
                 "algorithmic_bytes_per_launch": units, "kernel_us": kern_s * 1e6,
                 "note": "decode bytes over the decode kernel alone; its merge kernel is timed "
@@ -479,7 +521,7 @@ def main():
         achieved = units / kern_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                "traffic": measured_traffic("prefill", args.config),
+                "traffic": measured_traffic("prefill", name),
                 "kernel": "generic_kernel" if args.variant == "generic" else "prefill_pp_kernel",
                 "algorithmic_flops_per_launch": units, "kernel_us": kern_s * 1e6}
 
@@ -489,33 +531,36 @@ def main():
     else:
         metric, unit, value = "decode HBM GB/s (% of 8 TB/s)", "GB/s", B / step_s / 1e9
         frac_step = value / HBM_PEAK_GBS
-
+    res = {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms_per_step,
+           "config": {"workload": WORKLOADS[name], "name": name, "requests": b.num_reqs,
+                      "total_tokens": T, "context_tokens": int(b.context_lens.sum()),
+                      "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+                      "head_dim": b.head_dim, "page_size": b.page_size, "causal": b.causal,
+                      "variant": args.variant},
+           "tokens_per_s": T / step_s, "frac_of_peak_whole_step": frac_step,
+           "algorithmic_bytes": B, "algorithmic_flops": F,
+           "kernel_us": {k: v * 1e3 for k, v in stages.items()},
+           "step_us_single_calls": pctl(single)}
+    if dec and pre:
+        # Both rooflines on the whole (overlapped) call: the time the call
+        # would take at 8 TB/s for its bytes or at the bf16 peak for its
+        # FLOPs, whichever is longer, over the measured step.
+        t_min = max(B / (HBM_PEAK_GBS * 1e9), F / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+        res["mixed_roofline"] = {
+            "formula": "max(B / 8 TB/s, F / 2516.6 TFLOP/s) / t_step", "B": B, "F": F,
+            "t_us": ms_per_step * 1e3, "t_roofline_us": t_min * 1e6, "frac": t_min / step_s,
+            "frac_single_call_p50": t_min / (np.median(single) * 1e-6)}
+    if per_call:
+        res["flushed"] = flushed
+    res["roofline"] = roof
     cpu = None
-    if args.cpu_seconds > 0:
-        log(f"[bench] CPU baseline: oracle on a sample (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(b, "hbm" if unit == "GB/s" else "mfma", args.cpu_seconds)
-
-    line = {
-        "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "name": args.config,
-                   "requests": b.num_reqs, "total_tokens": T,
-                   "context_tokens": int(b.context_lens.sum()), "num_q_heads": b.num_q_heads,
-                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
-                   "page_size": b.page_size, "causal": b.causal, "variant": args.variant},
-        "tokens_per_s": T / step_s,
-        "frac_of_peak_whole_step": frac_step,
-        "algorithmic_bytes": B, "algorithmic_flops": F,
-        "kernel_us": {k: v * 1e3 for k, v in stages.items()},
-        "step_us_single_calls": pctl(single),
-        "flushed": flushed,
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "context": {"pages_decode_mbu_tpu7x": 0.86, "pages_prefill_mfu_tpu7x": 0.73,
-                    "pages_prefill_mfu_causal_tpu7x": 0.63},
-    }
-    print(json.dumps(line), flush=True)
+    if cpu_budget > 0:
+        log(f"[bench] {name}: CPU baseline: oracle on a sample (~{cpu_budget:.0f} s)")
+        cpu = cpu_baseline(b, "hbm" if unit == "GB/s" else "mfma", cpu_budget)
+    res["cpu_baseline"] = cpu
+    del call, dt
+    torch.cuda.synchronize()
+    return res
 
 
 if __name__ == "__main__":

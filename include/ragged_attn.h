@@ -37,7 +37,10 @@
  *   out          [T][Hq][D]             bf16, device, written
  *
  * Supported: D in {64, 128, 256}; S a multiple of 16, at most 1024 (the kernels
- * walk the cache in 16-row blocks of a page); Hq % Hkv == 0; Hq / Hkv <= 16;
+ * walk the cache in 16-row blocks of a page); any Hq / Hkv >= 1 with
+ * Hq % Hkv == 0 (decode rows run in blocks of 16 query heads per kv head;
+ * above 16 the cache pages a decode request reads are streamed once per
+ * block; prefill rows of groups above 256 heads run the generic kernel);
  * L_r < 2^30 (key positions are 32-bit inside the kernels).
  *
  * Ownership and concurrency: the caller owns every buffer, the workspace
@@ -47,8 +50,9 @@
  * never synchronises.  A batch with both decode and prefill requests runs
  * its prefill kernel on a second stream beside the decode kernel, forked
  * from and joined back into `stream` with events (capturable in a graph);
- * that stream and its two events are created per device on first use and
- * live until the process ends.  `out` must not alias any input.  A slot written by
+ * that stream and its two events are created per calling thread and device
+ * on first use and live until the process ends (so one thread's graph
+ * capture never absorbs another thread's eager calls).  `out` must not alias any input.  A slot written by
  * this call must not be read, as prior context, by any request of the same
  * call.  Two calls that share a workspace must be ordered on one stream.
  *
@@ -123,7 +127,13 @@ size_t ra_workspace_bytes(const ra_shape *shape, const int32_t *cu_q_lens_host,
  * ending at T, c_r >= 0, L_r <= max_pages_per_req * S); the full
  * O(T + pages) validation of page_table and slot_mapping is the separate
  * ra_validate_metadata.  A call whose page_table or slot_mapping break the
- * rules listed there is undefined.
+ * rules listed there, or whose device cu_q_lens / context_lens differ from
+ * the host copies, is undefined.  With RA_VALIDATE=1 in the environment the
+ * call first copies the device metadata to the host (synchronising on
+ * `stream`), checks that cu_q_lens and context_lens equal the host copies
+ * and runs ra_validate_metadata on it, returning RA_E_METADATA (nothing
+ * launched) on a violation; that mode refuses a stream under graph capture
+ * (RA_E_UNSUPPORTED).
  * Returns RA_OK once the work is enqueued on `stream`.
  */
 ra_status ra_forward(const ra_shape *shape,

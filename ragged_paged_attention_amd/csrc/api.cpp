@@ -40,13 +40,12 @@ ra_status check_shape(const ra_shape *s) {
                     s->num_q_heads, s->num_kv_heads);
     if (!(s->softmax_scale >= 0.f) || isinf(s->softmax_scale))
         return fail(RA_E_SHAPE, "softmax_scale must be finite and >= 0 (0 = 1/sqrt(D))");
-    const int D = s->head_dim, G = s->num_q_heads / s->num_kv_heads;
+    const int D = s->head_dim;
     if (!(D == 64 || D == 128 || D == 256))
         return fail(RA_E_UNSUPPORTED, "head_dim %d not supported (64, 128, 256)", D);
     if (s->page_size % 16 != 0 || s->page_size > 1024)
         return fail(RA_E_UNSUPPORTED, "page_size %d not supported (a multiple of 16, at most 1024)",
                     s->page_size);
-    if (G > 16) return fail(RA_E_UNSUPPORTED, "Hq/Hkv = %d above 16", G);
     const long long rows = (long long)s->num_pages * s->page_size * s->num_kv_heads * D;
     if (rows > (1LL << 40)) return fail(RA_E_UNSUPPORTED, "cache too large");
     return RA_OK;
@@ -71,6 +70,47 @@ ra_status check_host_lens(const ra_shape *s, const int32_t *cu, const int32_t *c
     if (cu[R] != s->total_tokens)
         return fail(RA_E_METADATA, "cu_q_lens[R] = %d but total_tokens = %d", cu[R], s->total_tokens);
     return RA_OK;
+}
+
+// RA_VALIDATE=1 (environment): copy the device metadata to the host (a
+// synchronising copy on the call's stream), check that cu_q_lens and
+// context_lens equal the host copies the dispatcher plans from, and run the
+// full ra_validate_metadata before anything is launched.
+ra_status validate_device_metadata(const ra_shape *s, const int32_t *page_table,
+                                   const int32_t *cu_q_lens, const int32_t *context_lens,
+                                   const int32_t *slot_mapping, const int32_t *cu_h,
+                                   const int32_t *ctx_h, hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+        return fail(RA_E_HIP, "RA_VALIDATE: hipStreamIsCapturing failed");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(RA_E_UNSUPPORTED, "RA_VALIDATE=1 copies the metadata to the host and cannot run "
+                                      "while the stream is being captured");
+    const int R = s->num_reqs, T = s->total_tokens;
+    std::vector<int32_t> pt((size_t)R * s->max_pages_per_req), cu((size_t)R + 1), ctx((size_t)R), sm((size_t)T);
+    auto get = [&](std::vector<int32_t> &dst, const int32_t *src) {
+        return dst.empty() ? hipSuccess
+                           : hipMemcpyAsync(dst.data(), src, dst.size() * sizeof(int32_t),
+                                            hipMemcpyDeviceToHost, stream);
+    };
+    hipError_t e = get(pt, page_table);
+    if (e == hipSuccess) e = get(cu, cu_q_lens);
+    if (e == hipSuccess) e = get(ctx, context_lens);
+    if (e == hipSuccess) e = get(sm, slot_mapping);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(RA_E_HIP, "RA_VALIDATE: metadata copy failed: %s", hipGetErrorString(e));
+    for (int r = 0; r <= R; ++r)
+        if (cu[r] != cu_h[r])
+            return fail(RA_E_METADATA, "device cu_q_lens[%d] = %d, host copy %d", r, cu[r], cu_h[r]);
+    for (int r = 0; r < R; ++r)
+        if (ctx[r] != ctx_h[r])
+            return fail(RA_E_METADATA, "device context_lens[%d] = %d, host copy %d", r, ctx[r], ctx_h[r]);
+    return ra_validate_metadata(s, pt.data(), cu.data(), ctx.data(), sm.data());
+}
+
+bool validate_requested() {
+    const char *v = getenv("RA_VALIDATE");
+    return v && v[0] == '1' && v[1] == '\0';
 }
 
 }  // namespace
@@ -137,12 +177,18 @@ ra_status ra_validate_metadata(const ra_shape *s, const int32_t *page_table,
     return RA_OK;
 }
 
-ra_status ra_forward_profiled(const ra_shape *s, const void *q, const void *k_new, const void *v_new,
-                              void *k_cache, void *v_cache, const int32_t *page_table,
-                              const int32_t *cu_q_lens, const int32_t *context_lens,
-                              const int32_t *slot_mapping, const int32_t *cu_h, const int32_t *ctx_h,
-                              void *out, void *workspace, size_t workspace_bytes, void *stream,
-                              int32_t variant, void *const *events, int32_t n_events) {
+}  // extern "C"
+
+namespace {
+
+// The fused call behind every forward entry point.  allow_side_stream lets
+// a mixed batch overlap its prefill kernel on a second stream.
+ra_status forward_impl(const ra_shape *s, const void *q, const void *k_new, const void *v_new,
+                       void *k_cache, void *v_cache, const int32_t *page_table,
+                       const int32_t *cu_q_lens, const int32_t *context_lens,
+                       const int32_t *slot_mapping, const int32_t *cu_h, const int32_t *ctx_h,
+                       void *out, void *workspace, size_t workspace_bytes, void *stream,
+                       int32_t variant, void *const *events, int32_t n_events, bool allow_side_stream) {
     g_last_error.clear();
     if (events && n_events != ra::kNumStageEvents)
         return fail(RA_E_SHAPE, "n_events must be %d", ra::kNumStageEvents);
@@ -171,6 +217,11 @@ ra_status ra_forward_profiled(const ra_shape *s, const void *q, const void *k_ne
     if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
         return fail(RA_E_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
     if (!has_tokens) return RA_OK;
+    if (validate_requested()) {
+        st = validate_device_metadata(s, page_table, cu_q_lens, context_lens, slot_mapping, cu_h, ctx_h,
+                                      (hipStream_t)stream);
+        if (st != RA_OK) return st;
+    }
 
     ra::Params p{};
     p.prefill_only = 0;
@@ -208,11 +259,26 @@ ra_status ra_forward_profiled(const ra_shape *s, const void *q, const void *k_ne
         for (int k = 2; k < ra::kNumStageEvents && err == hipSuccess; ++k) err = ev.record(k);
     } else {
         what = "specialised kernels";
-        err = ra::launch_plan(p, plan, workspace, hs, ev);
+        err = ra::launch_plan(p, plan, workspace, hs, ev, allow_side_stream);
     }
     if (err != hipSuccess)
         return fail(RA_E_HIP, "%s launch failed: %s", what, hipGetErrorString(err));
     return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_forward_profiled(const ra_shape *s, const void *q, const void *k_new, const void *v_new,
+                              void *k_cache, void *v_cache, const int32_t *page_table,
+                              const int32_t *cu_q_lens, const int32_t *context_lens,
+                              const int32_t *slot_mapping, const int32_t *cu_h, const int32_t *ctx_h,
+                              void *out, void *workspace, size_t workspace_bytes, void *stream,
+                              int32_t variant, void *const *events, int32_t n_events) {
+    return forward_impl(s, q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
+                        slot_mapping, cu_h, ctx_h, out, workspace, workspace_bytes, stream, variant,
+                        events, n_events, true);
 }
 
 ra_status ra_forward_variant(const ra_shape *s, const void *q, const void *k_new, const void *v_new,

@@ -16,7 +16,10 @@
 //
 // One wavefront per kv head; the G = Hq/Hkv query heads of a kv head share
 // every K/V byte its wavefront reads (grouped-query attention), so the cache
-// is read exactly once.  Per 16-token page:
+// is read exactly once when G <= 16.  Larger groups are cut into blocks of 16
+// query heads on the grid's third dimension: each block's workgroups stream
+// the same pages (the cache is then read ceil(G / 16) times).  Per 16-token
+// page:
 //   * the workgroup loads the page's K and V blocks of its HW heads with
 //     16-byte loads in address order (each token row holds the HW heads
 //     side by side, so a page arrives as 16 contiguous segments of up to
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n16 = lane & 15, kg = lane >> 4;
-    const int hg = blockIdx.x, b = blockIdx.y;
+    const int hg = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;  // hb: block of 16 query heads
     const int np = dw.np, nwg = dw.nwg;
     // The workgroup's flat pages [g0, g1): an equal share of all pages, or
     // (whole-request mode) the pages of an equal share of the requests.
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     if (dw.whole) {
         first_q = make_req(p, dw, x0, g0);
     } else if (dw.self_plan) {
-        const int2 f = self_plan_first(p, dw, g0, g1, hg == 0 && w == 0);
+        const int2 f = self_plan_first(p, dw, g0, g1, hg == 0 && hb == 0 && w == 0);
         first_q = make_req(p, dw, f.x, f.y);
     } else {
         const int first = ld_meta(dw.wstart, b);
@@ -387,10 +390,12 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     while (cq.pend == cq.pfx) cq = next_req(p, dw, cq);  // (a range may start at a request without pages)
     int seg_g = g0;  // first flat page of the current segment
     short8_t qb[KS];
-    // Q^T as the B operand: lane (head n16, group kg) holds q[t0][hk*G + n16][32ks + 8kg .. +8].
+    // This lane's query head inside the group (16 per head block).
+    const int gq = 16 * hb + n16;
+    const bool hv = gq < G;
+    // Q^T as the B operand: lane (head n16, group kg) holds q[t0][hk*G + gq][32ks + 8kg .. +8].
     auto load_q = [&]() {
-        const bool hv = n16 < G;
-        const bf16_t *qrow = p.q + ((size_t)cq.t0 * p.Hq + hk * G + (hv ? n16 : 0)) * D;
+        const bf16_t *qrow = p.q + ((size_t)cq.t0 * p.Hq + hk * G + (hv ? gq : 0)) * D;
         const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -481,8 +486,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         // (whole-request ranges never cut a request)
         const int b_first = dw.whole ? b : wg_of_page(cq.pfx, np, nwg);
         const int b_last = dw.whole ? b : wg_of_page(cq.pend - 1, np, nwg);
-        const bool hv = n16 < G;
-        const int h = hk * G + n16;  // q head
+        const int h = hk * G + gq;  // q head
         bf16_t *orow = p.out + ((size_t)cq.t0 * p.Hq + h) * D;
         if (b_first == b_last) {
             if (hv) {
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         // (a kernel boundary makes them visible without device-wide fences,
         // which flush the L2 of every XCD and would stall the streaming).
         if (hv) {
-            const size_t sidx = (size_t)partial_slot(hg, b, b_first, nwg) * (HW * G) + w * G + n16;
+            const size_t sidx = (size_t)partial_slot(hg, b, b_first, nwg) * (HW * G) + w * G + gq;
             float *prow = dw.part_o + sidx * D;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     // last page, scores/softmax/PV, and the end of the segment.
     auto step = [&](int g, int stage) {
         const int pr = g - cq.pfx;
-        if (g == cq.pend - 1 && lane < CPH && !p.skip_scatter) {
+        if (g == cq.pend - 1 && lane < CPH && hb == 0 && !p.skip_scatter) {
             // Fused KV-cache update of the new token (position c), this
             // wavefront's kv head: the row is in the LDS tile already (loaded
             // from k_new / v_new), so the copy waits on no global load.
@@ -589,48 +593,50 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n16 = lane & 15, kg = lane >> 4;
     const int G = p.Hq / p.Hkv;
-    if (n16 >= G) return;
-    const int hl = w * G + n16;  // q head inside the head group
-    // One pass with a running max; the slots are read kU at a time so that
-    // their loads are in flight together (a request rarely spans more than
-    // two or three workgroups).
-    constexpr int kU = 4;
-    float M = -INFINITY, den = 0.f;
-    float4_t acc[MB];
+    // Query heads n16, n16 + 16, ... of this wavefront's kv head.
+    for (int gq = n16; gq < G; gq += 16) {
+        const int hl = w * G + gq;  // q head inside the head group
+        // One pass with a running max; the slots are read kU at a time so
+        // that their loads are in flight together (a request rarely spans
+        // more than two or three workgroups).
+        constexpr int kU = 4;
+        float M = -INFINITY, den = 0.f;
+        float4_t acc[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    for (int b0 = b_first; b0 <= b_last; b0 += kU) {
-        float ms[kU], ls[kU];
-        float4_t os[kU][MB];
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int b0 = b_first; b0 <= b_last; b0 += kU) {
+            float ms[kU], ls[kU];
+            float4_t os[kU][MB];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int bb = min(b0 + u, b_last);
-            const size_t sidx = (size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl;
-            ms[u] = dw.part_ml[sidx * 2];
-            ls[u] = dw.part_ml[sidx * 2 + 1];
-            const float *prow = dw.part_o + sidx * D;
+            for (int u = 0; u < kU; ++u) {
+                const int bb = min(b0 + u, b_last);
+                const size_t sidx = (size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl;
+                ms[u] = dw.part_ml[sidx * 2];
+                ls[u] = dw.part_ml[sidx * 2 + 1];
+                const float *prow = dw.part_o + sidx * D;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) os[u][mb] = *reinterpret_cast<const float4_t *>(prow + 16 * mb + 4 * kg);
+                for (int mb = 0; mb < MB; ++mb) os[u][mb] = *reinterpret_cast<const float4_t *>(prow + 16 * mb + 4 * kg);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                if (b0 + u > b_last) break;
+                const float mn = fmaxf(M, ms[u]);
+                const float a = fast_exp2(M - mn), wgt = fast_exp2(ms[u] - mn);
+                den = den * a + wgt * ls[u];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) acc[mb] = acc[mb] * a + wgt * os[u][mb];
+                M = mn;
+            }
         }
+        const float inv = 1.f / den;
+        bf16_t *orow = p.out + ((size_t)t0 * p.Hq + (hg * HW + w) * G + gq) * D;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            if (b0 + u > b_last) break;
-            const float mn = fmaxf(M, ms[u]);
-            const float a = fast_exp2(M - mn), wgt = fast_exp2(ms[u] - mn);
-            den = den * a + wgt * ls[u];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) acc[mb] = acc[mb] * a + wgt * os[u][mb];
-            M = mn;
+        for (int mb = 0; mb < MB; ++mb) {
+            uint2 wv;
+            wv.x = cvt_pk_bf16(acc[mb][0] * inv, acc[mb][1] * inv);
+            wv.y = cvt_pk_bf16(acc[mb][2] * inv, acc[mb][3] * inv);
+            *reinterpret_cast<uint2 *>(orow + 16 * mb + 4 * kg) = wv;
         }
-    }
-    const float inv = 1.f / den;
-    bf16_t *orow = p.out + ((size_t)t0 * p.Hq + (hg * HW + w) * G + n16) * D;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        uint2 wv;
-        wv.x = cvt_pk_bf16(acc[mb][0] * inv, acc[mb][1] * inv);
-        wv.y = cvt_pk_bf16(acc[mb][2] * inv, acc[mb][3] * inv);
-        *reinterpret_cast<uint2 *>(orow + 16 * mb + 4 * kg) = wv;
     }
 }
 
@@ -668,7 +674,7 @@ hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t 
                              const StageEvents &ev) {
     hipError_t e = configure_decode<D, HW, PF>();
     if (e != hipSuccess) return e;
-    const dim3 grid(p.Hkv / HW, dw.nwg);
+    const dim3 grid(p.Hkv / HW, dw.nwg, (p.Hq / p.Hkv + 15) / 16);
     const size_t lds = DecodeCfg<D, HW>::LDS_BYTES;
     hipLaunchKernelGGL((decode_kernel<D, HW, PF>), grid, dim3(64 * HW), lds, stream, p, dw);
     e = hipGetLastError();
@@ -754,8 +760,11 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
     constexpr int kMinPages = 4;
     const char *env = getenv("RA_DECODE_WGS");
     const int forced = env ? atoi(env) : 0;
-    if (forced > 0) cap = forced * plan.decode_hgroups;
-    int n = std::max(1, cap / plan.decode_hgroups);
+    // Groups of more than 16 query heads launch one grid slice per block of
+    // 16 heads: together they fill the resident slots once.
+    const int hblocks = (p.Hq / p.Hkv + 15) / 16;
+    if (forced > 0) cap = forced * plan.decode_hgroups * hblocks;
+    int n = std::max(1, cap / (plan.decode_hgroups * hblocks));
     if (fill) *fill = n;  // workgroups per head group that fill every compute unit once
     n = std::min(n, plan.decode_wg_cap);
     n = std::min(n, whole > 0 ? whole : std::max(1, plan.n_decode_pages / kMinPages));

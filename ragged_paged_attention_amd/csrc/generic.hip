@@ -1,9 +1,10 @@
 // generic.hip -- the simple fused kernel: correct for every supported shape,
 // used as the GENERIC variant and as a cross-check of the specialised kernels.
 //
-// One wavefront per (new token t, kv head hk).  It first copies the token's
-// new K/V row of that head into its cache slot (the fused KV-cache update),
-// then computes exact attention for the G = Hq/Hkv query heads of the group
+// One wavefront per (new token t, kv head hk, block of up to 16 of the G =
+// Hq/Hkv query heads of the group).  The first block's wavefront copies the
+// token's new K/V row of that head into its cache slot (the fused KV-cache
+// update); every wavefront then computes exact attention for its query heads
 // with an online softmax over chunks of 64 keys, one key per lane:
 //   scores  : each lane dots its key row with the G query rows (fp32 VALU);
 //   softmax : chunk max / sum by wave reductions, running (m, l) per head;
@@ -26,6 +27,8 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
     const int hk = blockIdx.y;
     const int lane = threadIdx.x;
     const int G = p.Hq / p.Hkv;
+    const int hq0 = hk * G + kMaxG * blockIdx.z;  // first query head of this block
+    const int Gb = min(kMaxG, G - kMaxG * (int)blockIdx.z);  // query heads of this block
     const int D = p.D;
 
     const int r = request_of_token(p.cu_q_lens, p.R, t);
@@ -36,8 +39,8 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
     const int nvis = p.causal ? c + i + 1 : L;
     if (p.prefill_only && L - c == 1) return;
 
-    // KV-cache update for (t, hk).
-    {
+    // KV-cache update for (t, hk), by the first head block.
+    if (blockIdx.z == 0) {
         const size_t dst = ((size_t)p.slot_mapping[t] * p.Hkv + hk) * D;
         const size_t src = ((size_t)t * p.Hkv + hk) * D;
         for (int d = lane; d < D; d += 64) {
@@ -50,8 +53,8 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
     __shared__ float ps[kMaxG][64];
     __shared__ const bf16_t *vrows[64];
 
-    for (int g = 0; g < G; ++g) {
-        const bf16_t *qrow = p.q + ((size_t)t * p.Hq + hk * G + g) * D;
+    for (int g = 0; g < Gb; ++g) {
+        const bf16_t *qrow = p.q + ((size_t)t * p.Hq + hq0 + g) * D;
         for (int d = lane; d < D; d += 64) qs[g][d] = bf16_to_f32(qrow[d]);
     }
     __syncthreads();
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
                                      bf16_lo(kv.z), bf16_hi(kv.z), bf16_lo(kv.w), bf16_hi(kv.w)};
 #pragma unroll
                 for (int g = 0; g < kMaxG; ++g) {
-                    if (g < G) {
+                    if (g < Gb) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) s[g] += qs[g][d + e] * kf[e];
                     }
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
         vrows[lane] = vrow;
 #pragma unroll
         for (int g = 0; g < kMaxG; ++g) {
-            if (g < G) {
+            if (g < Gb) {
                 const float sg = valid ? s[g] * p.scale_log2 : -INFINITY;
                 const float mn = fmaxf(m[g], wave_max(sg));
                 const float alpha = fast_exp2(m[g] - mn);
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
                     const float vf = bf16_to_f32(vr[d]);
 #pragma unroll
                     for (int g = 0; g < kMaxG; ++g)
-                        if (g < G) acc[g][e] += ps[g][jj] * vf;
+                        if (g < Gb) acc[g][e] += ps[g][jj] * vf;
                 }
             }
         }
@@ -133,9 +136,9 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
 
 #pragma unroll
     for (int g = 0; g < kMaxG; ++g) {
-        if (g < G) {
+        if (g < Gb) {
             const float inv = 1.f / l[g];
-            bf16_t *orow = p.out + ((size_t)t * p.Hq + hk * G + g) * D;
+            bf16_t *orow = p.out + ((size_t)t * p.Hq + hq0 + g) * D;
 #pragma unroll
             for (int e = 0; e < kMaxD / 64; ++e) {
                 const int d = lane + 64 * e;
@@ -149,11 +152,11 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
 
 hipError_t launch_generic(const Params &p, hipStream_t stream) {
     if (p.T == 0) return hipSuccess;
-    dim3 grid(p.T, p.Hkv);
+    dim3 grid(p.T, p.Hkv, (p.Hq / p.Hkv + kMaxG - 1) / kMaxG);
     hipLaunchKernelGGL(generic_kernel, grid, dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
-bool generic_supports(int D, int G) { return D % 8 == 0 && D <= kMaxD && G <= kMaxG; }
+bool generic_supports(int D) { return D % 8 == 0 && D <= kMaxD; }
 
 }  // namespace ra

@@ -8,6 +8,6 @@
 namespace ra {
 
 hipError_t launch_generic(const Params &p, hipStream_t stream);
-bool generic_supports(int D, int G);
+bool generic_supports(int D);
 
 }  // namespace ra

@@ -4,7 +4,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <mutex>
 
 #include "launch.hpp"
 #include "plan.hpp"
@@ -40,7 +39,9 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     pl.decode_hgroups = Hkv / pl.decode_hw;
     pl.decode_wg_cap = pl.n_decode_reqs ? std::max(1, kMaxDecodeWorkgroups / pl.decode_hgroups) : 0;
     pl.q_tile = prefill_supports(D, G) ? prefill_rows(D) / G : 0;
-    pl.specialised_ok = (s.page_size % 16 == 0) && (D == 64 || D == 128 || D == 256) && G <= 16 &&
+    // The decode kernel takes any group size (blocks of 16 query heads), the
+    // prefill kernel up to 256.
+    pl.specialised_ok = (s.page_size % 16 == 0) && (D == 64 || D == 128 || D == 256) &&
                         (pl.n_prefill_reqs == 0 || pl.q_tile > 0);
     double dec_bytes = 0, pre_flops = 0;
     for (int r = 0; r < R; ++r) {
@@ -137,9 +138,11 @@ __device__ int last_le(P a, int n, int x) {
 // per-request prefix of prefill items and the prefill items themselves
 // (longest query tiles of a request first; two int4 per item:
 // {r, kv head, first query, first token}, {context, new tokens, 0, 0}).
-// Mirrors make_plan.
+// Mirrors make_plan.  At most max_items items are written: the workspace
+// holds that many (the count the host planned from its copies of the same
+// metadata).
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    const int32_t *cu, const int32_t *ctx, int R, int S, int q_tile, int Hkv, int nwg,
+    const int32_t *cu, const int32_t *ctx, int R, int S, int q_tile, int Hkv, int nwg, int max_items,
     int32_t *dreq, int32_t *dpfx, int32_t *wstart, int32_t *ppfx, int4 *pre) {
     __shared__ int buf[3][kPlanThreads];
     __shared__ int dpfx_l[kPlanLds + 1], ppfx_l[kPlanLds + 1];  // LDS copies for the searches
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         const int g0 = (int)(((long long)b * np) / nwg);
         wstart[b] = nd <= kPlanLds ? last_le(dpfx_l, nd + 1, g0) : last_le(dpfx, nd + 1, g0);
     }
-    for (int k = tid; k < npre; k += kPlanThreads) {
+    for (int k = tid; k < min(npre, max_items); k += kPlanThreads) {
         const int r = R <= kPlanLds ? last_le(ppfx_l, R + 1, k) : last_le(ppfx, R + 1, k);
         const int p0 = R <= kPlanLds ? ppfx_l[r] : ppfx[r];
         const int p1 = R <= kPlanLds ? ppfx_l[r + 1] : ppfx[r + 1];
@@ -215,16 +218,15 @@ __global__ __launch_bounds__(256) void scatter_kernel(Params p) {
 
 // Concurrent mixed batches: the prefill kernel runs on a second stream next
 // to the decode kernel (MFMA-bound and HBM-bound work on different compute
-// units).  One side stream and two fork/join events per device, created on
-// first use and kept until the process ends; a mutex keeps the record / wait
-// sequence of concurrent callers apart.
+// units).  One side stream and two fork/join events per calling thread and
+// device, created on first use and kept until the process ends, so a thread
+// that captures a graph and a thread that launches eagerly never share them.
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
 };
 
-std::mutex g_side_mu;
-SideStream g_side[64];
+thread_local SideStream g_side[64];
 
 hipError_t side_stream(SideStream **out) {
     int dev = 0;
@@ -283,7 +285,7 @@ int env_int(const char *name, int dflt) {
 }  // namespace
 
 hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipStream_t stream,
-                       const StageEvents &ev) {
+                       const StageEvents &ev, bool allow_overlap) {
     char *w = (char *)workspace;
     DecodeWork dw;
     dw.dreq = (const int32_t *)(w + plan.off_dreq);
@@ -320,7 +322,8 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     // A batch with both kinds of work runs its prefill kernel beside the
     // decode kernel (not when the caller times the stages), and the decode
     // kernel then leaves part of the compute units to it at first.
-    const bool overlap = !ev.events && has_decode && has_prefill && env_int("RA_MIXED_OVERLAP", 1) != 0;
+    const bool overlap = allow_overlap && !ev.events && has_decode && has_prefill &&
+                         env_int("RA_MIXED_OVERLAP", 1) != 0;
     if (has_decode) {
         int fill = 0, cus = 0;
         err = decode_workgroups(p, plan, dw.whole ? dw.nd : 0, &dw.nwg, &fill, &cus);
@@ -352,7 +355,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     }
     if (!self_plan) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
-                           p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg,
+                           p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg, plan.n_prefill_items,
                            (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
                            (int32_t *)(w + plan.off_ppfx), pre);
         err = hipGetLastError();
@@ -360,7 +363,6 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     }
     if (overlap) {
         SideStream *ss = nullptr;
-        std::lock_guard<std::mutex> lock(g_side_mu);
         err = side_stream(&ss);
         // The decode kernel is queued first so that its (persistent)
         // workgroups take their compute units before the prefill items do.

@@ -228,8 +228,11 @@ struct StageEvents {
 
 void make_plan(const ra_shape &s, const int32_t *cu_h, const int32_t *ctx_h, Plan *plan);
 
+// allow_overlap: a mixed batch may run its prefill kernel on the calling
+// thread's side stream beside the decode kernel (otherwise the kernels run
+// one after the other on `stream`).
 hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipStream_t stream,
-                       const StageEvents &ev);
+                       const StageEvents &ev, bool allow_overlap);
 
 // Kernels of the specialised path.
 // kv heads per decode workgroup for this head_dim, kv-head count and batch

@@ -672,7 +672,10 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
 
 }  // namespace
 
-bool prefill_supports(int D, int G) { return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16; }
+// A workgroup's 256 rows hold floor(256 / G) tokens of each of the G query
+// heads, so groups of up to 256 heads fit (larger groups run the generic
+// kernel).
+bool prefill_supports(int D, int G) { return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 256; }
 
 int prefill_rows(int D) {
     switch (D) {

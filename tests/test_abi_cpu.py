@@ -137,7 +137,6 @@ def test_forward_rejects_before_touching_the_gpu(lib):
     cu, ctx = b.cu_q_lens.clone(), b.context_lens.clone()
     assert _forward_status(lib, shape_for(b, head_dim=96), cu, ctx) == 3  # unsupported
     assert _forward_status(lib, shape_for(b, page_size=24), cu, ctx) == 3  # not a multiple of 16
-    assert _forward_status(lib, shape_for(b, num_q_heads=64, num_kv_heads=2), cu, ctx) == 3  # G = 32 > 16
     assert _forward_status(lib, shape_for(b, page_size=2048), cu, ctx) == 3  # page above 1024
     assert _forward_status(lib, shape_for(b, num_kv_heads=3), cu, ctx) == 2
     assert _forward_status(lib, shape_for(b), cu, ctx, ws_bytes=16) == 5  # workspace too small
@@ -149,6 +148,17 @@ def test_forward_rejects_before_touching_the_gpu(lib):
     assert _forward_status(lib, shape_for(b, scale=float("inf")), cu, ctx) == 2
     huge = ctx.clone(); huge[0] = 1 << 30  # key positions are 32-bit inside the kernels
     assert _forward_status(lib, shape_for(b, max_pages_per_req=1 << 27), cu, huge) == 3
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (64, 2), (300, 1), (48, 3)])
+def test_any_group_size_is_accepted(lib, hq, hkv):
+    """Any G = Hq / Hkv >= 1 passes the host checks and gets a workspace
+    (decode heads go in blocks of 16, prefill rows up to G = 256, the
+    generic kernel beyond that)."""
+    b = random_batch(9, num_reqs=5, max_q=40, max_ctx=200, num_q_heads=hq, num_kv_heads=hkv,
+                     head_dim=64, decode_frac=0.5)
+    assert validate(b) == "RA_OK"
+    assert binding.workspace_bytes(shape_for(b), b.cu_q_lens, b.context_lens) > 0
 
 
 def test_empty_batch_is_a_no_op(lib):

@@ -170,6 +170,54 @@ def test_few_key_prefill_rows(case):
     check_small(b, "specialised")
 
 
+LARGE_G = [
+    # (seed, R, max_q, max_ctx, Hq, Hkv, D, decode_frac, causal)
+    (71, 6, 60, 300, 32, 1, 128, 0.5, True),    # G = 32 (one kv head), mixed
+    (72, 5, 1, 900, 64, 2, 64, 1.0, True),      # G = 32, decode only
+    (73, 4, 90, 100, 64, 1, 256, 0.0, True),    # G = 64, prefill only (4 tokens per item)
+    (74, 6, 50, 500, 128, 2, 128, 0.5, False),  # G = 64, mixed, non-causal
+    (75, 5, 40, 120, 40, 2, 64, 0.5, True),     # G = 20 (12 tokens per item, 16 idle rows)
+    (76, 3, 20, 100, 300, 1, 64, 0.5, True),    # G = 300: prefill rows in the generic kernel
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("case", LARGE_G, ids=lambda c: f"G{c[4] // c[5]}-s{c[0]}")
+def test_large_groups(case, variant):
+    """Groups of more than 16 query heads per kv head: the decode kernel takes
+    them in blocks of 16 heads, the prefill kernel as floor(256 / G) tokens of
+    G heads per item, and the generic kernel in blocks of 16 heads."""
+    seed, R, mq, mc, Hq, Hkv, D, frac, causal = case
+    b = random_batch(seed, num_reqs=R, max_q=mq, max_ctx=mc, num_q_heads=Hq, num_kv_heads=Hkv,
+                     head_dim=D, decode_frac=frac, causal=causal)
+    check_small(b, variant)
+
+
+def test_validate_switch_checks_device_metadata(monkeypatch):
+    """RA_VALIDATE=1: the call copies the device metadata back, compares it
+    with the host copies and runs the full validation before any launch; a
+    slot_mapping that disagrees with the page table, or a host copy that
+    disagrees with the device, is refused (RA_E_METADATA) and nothing runs."""
+    monkeypatch.setenv("RA_VALIDATE", "1")
+    b = random_batch(77, num_reqs=6, max_q=40, max_ctx=300, num_q_heads=16, num_kv_heads=4,
+                     head_dim=128, decode_frac=0.5)
+    check_small(b, "specialised")
+    dev = torch.device("cuda:0")
+    args = [t.to(dev) for t in (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
+                                b.cu_q_lens, b.context_lens, b.slot_mapping)]
+    sm = args[8].clone()
+    sm[0] = sm[-1]
+    sentinel = torch.full_like(args[0], 7.0)
+    for bad_args, cu_h, ctx_h in ((args[:8] + [sm], b.cu_q_lens, b.context_lens),
+                                  (args, b.cu_q_lens, b.context_lens - (b.context_lens > 0).int())):
+        with pytest.raises(binding.RaError) as e:
+            binding.forward(*bad_args, causal=b.causal, out=sentinel, cu_q_lens_host=cu_h,
+                            context_lens_host=ctx_h)
+        assert e.value.name == "RA_E_METADATA", str(e.value)
+        torch.cuda.synchronize()
+        assert bool((sentinel == 7.0).all()), "a refused call wrote its output"
+
+
 PAGED = [
     # (seed, S, R, max_q, max_ctx, Hq, Hkv, D, decode_frac, causal)
     (31, 32, 6, 70, 300, 32, 8, 128, 0.5, True),
