@@ -176,6 +176,31 @@ ra_status ra_forward_profiled(const ra_shape *shape,
                               int32_t variant, void *const *events, int32_t n_events);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ra_forward
+ * without a workspace argument.  Its work lists and decode partials live in a
+ * static device array of 64 MiB that each device the library runs on holds
+ * from the library's load until the process ends (the address is looked up
+ * once per device, on the first call with that device current).  A batch
+ * whose ra_workspace_bytes() exceeds 64 MiB is refused with RA_E_WORKSPACE
+ * before anything is launched (Llama-3-8B shapes need about 17 MB whatever
+ * the batch's context lengths).  The call allocates nothing itself: a batch
+ * with both decode and prefill requests runs its kernels one after the other
+ * on `stream`, without the side stream ra_forward may create.  All calls on
+ * one device share the array and each call overwrites what the last one left
+ * there (its contents on entry do not matter): calls that may overlap on one
+ * device (different streams or threads) race, and the caller must order them.
+ * Otherwise as ra_forward (same arguments, checks and results).
+ */
+ra_status ra_forward_noalloc(const ra_shape *shape,
+                             const void *q, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache,
+                             const int32_t *page_table, const int32_t *cu_q_lens,
+                             const int32_t *context_lens, const int32_t *slot_mapping,
+                             const int32_t *cu_q_lens_host, const int32_t *context_lens_host,
+                             void *out, void *stream);
+
+/*
  * Full metadata validation on host copies; touches no GPU.  Checks:
  * cu_q_lens[0] == 0, non-decreasing, cu_q_lens[R] == T; c_r >= 0;
  * L_r <= max_pages_per_req * S; the first ceil(L_r / S) page-table entries of

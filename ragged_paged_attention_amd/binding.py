@@ -63,6 +63,8 @@ def load_library():
     lib.ra_forward_variant.argtypes = fwd_args + [i32]
     lib.ra_forward_profiled.restype = i32
     lib.ra_forward_profiled.argtypes = fwd_args + [i32, P, i32]
+    lib.ra_forward_noalloc.restype = i32
+    lib.ra_forward_noalloc.argtypes = [shp, P, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.ra_validate_metadata.restype = i32
     lib.ra_validate_metadata.argtypes = [shp, P, P, P, P]
     lib.ra_status_str.restype = ctypes.c_char_p
@@ -154,6 +156,28 @@ def forward(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_le
         _ptr(page_table), _ptr(cu_q_lens), _ptr(context_lens), _ptr(slot_mapping), _ptr(cu_h),
         _ptr(ctx_h), _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
         ctypes.c_void_p(stream), VARIANTS[variant])
+    _check(status)
+    return out
+
+
+def forward_noalloc(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
+                    slot_mapping, *, causal=True, scale=None, out=None, cu_q_lens_host=None,
+                    context_lens_host=None, stream=None):
+    """forward() through ra_forward_noalloc: no workspace (the library's static
+    scratch array serves), no allocation inside the call.  `out` is allocated
+    here when not given (that is the caller's memory, not the call's)."""
+    lib = load_library()
+    shape = shape_of(q, k_cache, page_table, context_lens, scale=scale, causal=causal)
+    cu_h = _host_i32(cu_q_lens if cu_q_lens_host is None else cu_q_lens_host)
+    ctx_h = _host_i32(context_lens if context_lens_host is None else context_lens_host)
+    if out is None:
+        out = torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    status = lib.ra_forward_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+        _ptr(page_table), _ptr(cu_q_lens), _ptr(context_lens), _ptr(slot_mapping), _ptr(cu_h),
+        _ptr(ctx_h), _ptr(out), ctypes.c_void_p(stream))
     _check(status)
     return out
 

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -300,6 +301,79 @@ ra_status ra_forward(const ra_shape *s, const void *q, const void *k_new, const 
     return ra_forward_variant(s, q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens,
                               context_lens, slot_mapping, cu_h, ctx_h, out, workspace,
                               workspace_bytes, stream, RA_VARIANT_AUTO);
+}
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: its workspace is a static device
+// array of kScratchBytes (each device the library runs on holds its own copy
+// from module load until the process ends).
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+
+}  // namespace
+
+// Host code must not pass this name to a kernel: it stands for the host-side
+// shadow of the array.  The device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // per device, set once
+
+// Device address of `scratch` on the current device (looked up once per
+// device, with that device current).
+ra_status scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RA_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(RA_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(RA_E_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_forward_noalloc(const ra_shape *s, const void *q, const void *k_new, const void *v_new,
+                             void *k_cache, void *v_cache, const int32_t *page_table,
+                             const int32_t *cu_q_lens, const int32_t *context_lens,
+                             const int32_t *slot_mapping, const int32_t *cu_h, const int32_t *ctx_h,
+                             void *out, void *stream) {
+    g_last_error.clear();
+    ra_status st = check_shape(s);
+    if (st != RA_OK) return st;
+    st = check_host_lens(s, cu_h, ctx_h);
+    if (st != RA_OK) return st;
+    ra::Plan plan;
+    ra::make_plan(*s, cu_h, ctx_h, &plan);
+    if (plan.workspace_bytes > kScratchBytes)
+        return fail(RA_E_WORKSPACE, "the batch needs %zu bytes of workspace; the static scratch holds %zu",
+                    plan.workspace_bytes, kScratchBytes);
+    void *ws = nullptr;
+    if (plan.workspace_bytes > 0) {
+        st = scratch_address(&ws);
+        if (st != RA_OK) return st;
+    }
+    // No side stream (creating one allocates): a mixed batch runs its
+    // kernels one after the other on `stream`.
+    return forward_impl(s, q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
+                        slot_mapping, cu_h, ctx_h, out, ws, kScratchBytes, stream, RA_VARIANT_AUTO,
+                        nullptr, 0, false);
 }
 
 }  // extern "C"
