@@ -110,8 +110,10 @@ typedef enum {
  * Bytes of device workspace ra_forward needs for this batch (work lists,
  * merge counters and the partial results of decode requests that several
  * workgroups share).  Host copies of cu_q_lens [R+1] and context_lens [R]
- * are read.  Returns 0 when the shape is invalid.  The size does not depend
- * on the variant.
+ * are read; with both NULL the result is the bound that covers every batch
+ * of the shape's R requests and T new tokens (planning on the device, see
+ * ra_forward).  Returns 0 when the shape is invalid or only one host copy is
+ * given.  The size does not depend on the variant.
  */
 size_t ra_workspace_bytes(const ra_shape *shape, const int32_t *cu_q_lens_host,
                           const int32_t *context_lens_host);
@@ -120,7 +122,15 @@ size_t ra_workspace_bytes(const ra_shape *shape, const int32_t *cu_q_lens_host,
  * The fused call: KV-cache update plus attention, as defined above.
  *
  * cu_q_lens_host / context_lens_host: host copies of the device metadata;
- * they must hold the same values (the dispatcher plans from them).
+ * they must hold the same values (the dispatcher plans from them).  Both
+ * NULL: the call plans on the device instead (the analogue of the pages'
+ * metadata offload, talk summary 00:16:06): a one-workgroup plan kernel
+ * builds the work lists and counts from the device metadata, and every grid
+ * is sized from the bounds R = num_reqs and T = total_tokens, so no launch
+ * parameter depends on the lengths and a call captured in a graph stays
+ * valid for any batch of R requests and T new tokens (the workspace then
+ * needs ra_workspace_bytes(shape, NULL, NULL)).  A mixed batch then runs its
+ * kernels one after the other.
  * workspace: device memory of at least ra_workspace_bytes() bytes, 256-byte
  * aligned; its contents on entry do not matter.
  * Checks are O(1) plus O(R) over the host metadata (cu_q_lens monotone and

@@ -109,9 +109,13 @@ def shape_of(q, k_cache, page_table, context_lens, *, scale=None, causal=True) -
                       causal=causal)
 
 
-def workspace_bytes(shape: RaShape, cu_q_lens_host: torch.Tensor,
-                    context_lens_host: torch.Tensor) -> int:
+def workspace_bytes(shape: RaShape, cu_q_lens_host: torch.Tensor | None,
+                    context_lens_host: torch.Tensor | None) -> int:
+    """Workspace for a batch; with both host copies None, the bound for any
+    batch of the shape's R requests and T tokens (planning on the device)."""
     lib = load_library()
+    if cu_q_lens_host is None and context_lens_host is None:
+        return int(lib.ra_workspace_bytes(ctypes.byref(shape), None, None))
     cu, ctx = _host_i32(cu_q_lens_host), _host_i32(context_lens_host)
     return int(lib.ra_workspace_bytes(ctypes.byref(shape), _ptr(cu), _ptr(ctx)))
 
@@ -125,12 +129,16 @@ def validate_metadata(shape: RaShape, page_table, cu_q_lens, context_lens, slot_
 
 def forward(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
             slot_mapping, *, causal=True, scale=None, out=None, cu_q_lens_host=None,
-            context_lens_host=None, workspace=None, variant="auto", stream=None):
+            context_lens_host=None, workspace=None, variant="auto", stream=None,
+            plan_on_device=False):
     """Fused KV-cache update + ragged paged attention on the current stream.
 
     All tensors live on the GPU except the optional host copies of cu_q_lens
     and context_lens (taken from the device tensors when not given, which
-    synchronises).  k_cache / v_cache are updated in place; returns `out`.
+    synchronises).  plan_on_device=True passes no host copies: the library
+    plans from the bounds R = len(context_lens) and T = len(q) on the device,
+    so nothing is synchronised and a captured graph stays valid when the
+    lengths change.  k_cache / v_cache are updated in place; returns `out`.
     """
     lib = load_library()
     for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
@@ -142,8 +150,11 @@ def forward(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_le
         if t.dtype != torch.int32 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous int32 tensor")
     shape = shape_of(q, k_cache, page_table, context_lens, scale=scale, causal=causal)
-    cu_h = _host_i32(cu_q_lens if cu_q_lens_host is None else cu_q_lens_host)
-    ctx_h = _host_i32(context_lens if context_lens_host is None else context_lens_host)
+    if plan_on_device:
+        cu_h = ctx_h = None
+    else:
+        cu_h = _host_i32(cu_q_lens if cu_q_lens_host is None else cu_q_lens_host)
+        ctx_h = _host_i32(context_lens if context_lens_host is None else context_lens_host)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
@@ -162,14 +173,17 @@ def forward(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_le
 
 def forward_noalloc(q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
                     slot_mapping, *, causal=True, scale=None, out=None, cu_q_lens_host=None,
-                    context_lens_host=None, stream=None):
+                    context_lens_host=None, stream=None, plan_on_device=False):
     """forward() through ra_forward_noalloc: no workspace (the library's static
     scratch array serves), no allocation inside the call.  `out` is allocated
     here when not given (that is the caller's memory, not the call's)."""
     lib = load_library()
     shape = shape_of(q, k_cache, page_table, context_lens, scale=scale, causal=causal)
-    cu_h = _host_i32(cu_q_lens if cu_q_lens_host is None else cu_q_lens_host)
-    ctx_h = _host_i32(context_lens if context_lens_host is None else context_lens_host)
+    if plan_on_device:
+        cu_h = ctx_h = None
+    else:
+        cu_h = _host_i32(cu_q_lens if cu_q_lens_host is None else cu_q_lens_host)
+        ctx_h = _host_i32(context_lens if context_lens_host is None else context_lens_host)
     if out is None:
         out = torch.empty_like(q)
     if stream is None:

@@ -52,9 +52,11 @@ ra_status check_shape(const ra_shape *s) {
     return RA_OK;
 }
 
-// O(R) checks of the host copies of cu_q_lens and context_lens.
+// O(R) checks of the host copies of cu_q_lens and context_lens.  Both NULL
+// means planning on the device from the bounds R and T (nothing to check).
 ra_status check_host_lens(const ra_shape *s, const int32_t *cu, const int32_t *ctx) {
-    if (!cu || !ctx) return fail(RA_E_NULL, "host cu_q_lens / context_lens are NULL");
+    if (!cu && !ctx) return RA_OK;
+    if (!cu || !ctx) return fail(RA_E_NULL, "give both host copies (cu_q_lens, context_lens) or neither");
     const int R = s->num_reqs;
     if (cu[0] != 0) return fail(RA_E_METADATA, "cu_q_lens[0] = %d, must be 0", cu[0]);
     for (int r = 0; r < R; ++r) {
@@ -100,10 +102,10 @@ ra_status validate_device_metadata(const ra_shape *s, const int32_t *page_table,
     if (e == hipSuccess) e = get(sm, slot_mapping);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return fail(RA_E_HIP, "RA_VALIDATE: metadata copy failed: %s", hipGetErrorString(e));
-    for (int r = 0; r <= R; ++r)
+    for (int r = 0; r <= R && cu_h; ++r)
         if (cu[r] != cu_h[r])
             return fail(RA_E_METADATA, "device cu_q_lens[%d] = %d, host copy %d", r, cu[r], cu_h[r]);
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R && ctx_h; ++r)
         if (ctx[r] != ctx_h[r])
             return fail(RA_E_METADATA, "device context_lens[%d] = %d, host copy %d", r, ctx[r], ctx_h[r]);
     return ra_validate_metadata(s, pt.data(), cu.data(), ctx.data(), sm.data());

@@ -265,7 +265,11 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n16 = lane & 15, kg = lane >> 4;
     const int hg = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;  // hb: block of 16 query heads
-    const int np = dw.np, nwg = dw.nwg;
+    // (planning on the device: the page and workgroup counts the plan
+    // kernel wrote; the launched workgroups past them have nothing to do)
+    const int np = dw.counts ? ld_meta(dw.counts, 1) : dw.np;
+    const int nwg = dw.counts ? ld_meta(dw.counts, 3) : dw.nwg;
+    if (b >= nwg) return;
     // The workgroup's flat pages [g0, g1): an equal share of all pages, or
     // (whole-request mode) the pages of an equal share of the requests.
     int g0, g1, x0 = 0;
@@ -583,12 +587,17 @@ template <int D, int HW>
 __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeWork dw) {
     constexpr int MB = D / 16;
     const int i = blockIdx.x, hg = blockIdx.y;  // (requests on x: more than 65535 of them fit)
+    // Planning on the device: the grid covers every request, the list holds
+    // counts[0] decode requests.
+    if (dw.counts && i >= ld_meta(dw.counts, 0)) return;
+    const int np = dw.counts ? ld_meta(dw.counts, 1) : dw.np;
+    const int nwg = dw.counts ? ld_meta(dw.counts, 3) : dw.nwg;
     const int r = dw.self_plan ? i : ld_meta(dw.dreq, i);
     const int t0 = ld_meta(p.cu_q_lens, r);
     if (dw.self_plan && ld_meta(p.cu_q_lens, r + 1) - t0 != 1) return;  // not a decode request
     const int pfx = ld_meta(dw.dpfx, i), pend = pfx + blocks_of(ld_meta(p.context_lens, r));
-    const int b_first = wg_of_page(pfx, dw.np, dw.nwg);
-    const int b_last = wg_of_page(pend - 1, dw.np, dw.nwg);
+    const int b_first = wg_of_page(pfx, np, nwg);
+    const int b_last = wg_of_page(pend - 1, np, nwg);
     if (b_first == b_last) return;  // written by the decode kernel
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n16 = lane & 15, kg = lane >> 4;
@@ -610,7 +619,7 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int bb = min(b0 + u, b_last);
-                const size_t sidx = (size_t)partial_slot(hg, bb, b_first, dw.nwg) * (HW * G) + hl;
+                const size_t sidx = (size_t)partial_slot(hg, bb, b_first, nwg) * (HW * G) + hl;
                 ms[u] = dw.part_ml[sidx * 2];
                 ls[u] = dw.part_ml[sidx * 2 + 1];
                 const float *prow = dw.part_o + sidx * D;
@@ -755,9 +764,8 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
         if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
     }
-    // One resident wave of workgroups, none with fewer than kMinPages pages.
+    // One resident wave of workgroups, none with fewer than kMinDecodePages pages.
     // RA_DECODE_WGS (environment) overrides the resident count, for tuning.
-    constexpr int kMinPages = 4;
     const char *env = getenv("RA_DECODE_WGS");
     const int forced = env ? atoi(env) : 0;
     // Groups of more than 16 query heads launch one grid slice per block of
@@ -767,7 +775,9 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
     int n = std::max(1, cap / (plan.decode_hgroups * hblocks));
     if (fill) *fill = n;  // workgroups per head group that fill every compute unit once
     n = std::min(n, plan.decode_wg_cap);
-    n = std::min(n, whole > 0 ? whole : std::max(1, plan.n_decode_pages / kMinPages));
+    // (planning on the device: the page count is unknown here; workgroups
+    // whose range is empty exit at once)
+    if (!plan.bounds) n = std::min(n, whole > 0 ? whole : std::max(1, plan.n_decode_pages / kMinDecodePages));
     *nwg = n;
     return hipSuccess;
 }

@@ -22,8 +22,9 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     Plan pl;
     const int R = s.num_reqs, Hq = s.num_q_heads, Hkv = s.num_kv_heads, D = s.head_dim;
     const int G = Hq / Hkv;
+    pl.bounds = !cu || !ctx;
     long long np = 0;
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < R && !pl.bounds; ++r) {
         const int q = cu[r + 1] - cu[r];
         if (q == 1) {
             ++pl.n_decode_reqs;
@@ -35,7 +36,13 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
         }
     }
     pl.n_decode_pages = (int)np;
-    pl.decode_hw = decode_heads_per_group(D, Hkv, np, pl.n_decode_reqs);
+    if (pl.bounds) {
+        // Every request may be a decode request or a prefill chunk.
+        pl.n_decode_reqs = R;
+        pl.n_prefill_reqs = R;
+    }
+    pl.decode_hw = pl.bounds ? decode_heads_per_group(D, Hkv, 0, 0)
+                             : decode_heads_per_group(D, Hkv, np, pl.n_decode_reqs);
     pl.decode_hgroups = Hkv / pl.decode_hw;
     pl.decode_wg_cap = pl.n_decode_reqs ? std::max(1, kMaxDecodeWorkgroups / pl.decode_hgroups) : 0;
     pl.q_tile = prefill_supports(D, G) ? prefill_rows(D) / G : 0;
@@ -44,7 +51,15 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     pl.specialised_ok = (s.page_size % 16 == 0) && (D == 64 || D == 128 || D == 256) &&
                         (pl.n_prefill_reqs == 0 || pl.q_tile > 0);
     double dec_bytes = 0, pre_flops = 0;
-    for (int r = 0; r < R; ++r) {
+    if (pl.bounds && pl.q_tile > 0) {
+        // Chunks of q >= 2 tokens: sum over them of ceil(q / q_tile) is at
+        // most T / q_tile + (their number), and there are at most
+        // min(R, T / 2) of them.
+        const long long T = s.total_tokens;
+        const long long tiles = (T + pl.q_tile - 1) / pl.q_tile + std::min<long long>(R, T / 2);
+        pl.n_prefill_items = (int)std::min<long long>(tiles * Hkv, 1LL << 30);
+    }
+    for (int r = 0; r < R && !pl.bounds; ++r) {
         const int q = cu[r + 1] - cu[r];
         if (q > 1 && pl.q_tile > 0) pl.n_prefill_items += (int)ceil_div(q, pl.q_tile) * Hkv;
         if (q == 1) dec_bytes += (double)(ctx[r] + 1) * Hkv * D * 4;
@@ -88,6 +103,8 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     off = align256(off + sizeof(int32_t) * ((size_t)R + 1));
     pl.off_prefill = off;
     off = align256(off + 2 * sizeof(int4) * (size_t)pl.n_prefill_items);
+    pl.off_counts = off;
+    off = align256(off + sizeof(int32_t) * (pl.bounds ? 4 : 0));
     // A batch without new tokens launches nothing and needs no workspace.
     pl.workspace_bytes = (nd == 0 && pl.n_prefill_reqs == 0) ? 0 : off;
     *plan = pl;
@@ -143,7 +160,7 @@ __device__ int last_le(P a, int n, int x) {
 // metadata).
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t *cu, const int32_t *ctx, int R, int S, int q_tile, int Hkv, int nwg, int max_items,
-    int32_t *dreq, int32_t *dpfx, int32_t *wstart, int32_t *ppfx, int4 *pre) {
+    int32_t *dreq, int32_t *dpfx, int32_t *wstart, int32_t *ppfx, int4 *pre, int32_t *counts) {
     __shared__ int buf[3][kPlanThreads];
     __shared__ int dpfx_l[kPlanLds + 1], ppfx_l[kPlanLds + 1];  // LDS copies for the searches
     const int tid = threadIdx.x;
@@ -175,7 +192,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         for (int k = 0; k < 3; ++k) base[k] += tot[k];
     }
     const int nd = base[0], np = base[1], npre = base[2];
+    // Planning on the device: the decode grid was sized from bounds; only
+    // the first nwg of its workgroups per head group take pages, so that
+    // none between a request's first and last is empty.
+    if (counts) nwg = max(1, min(nwg, np / kMinDecodePages));
     if (tid == 0) {
+        if (counts) {  // planning on the device: the kernels read the real counts
+            counts[0] = nd;
+            counts[1] = np;
+            counts[2] = min(npre, max_items);
+            counts[3] = nwg;
+        }
         dpfx[nd] = np;
         ppfx[R] = npre;
         if (nd <= kPlanLds) dpfx_l[nd] = np;
@@ -297,6 +324,9 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
     dw.hw = plan.decode_hw;
+    // Planning on the device: the plan kernel writes the real counts here,
+    // and every grid below is sized from bounds.
+    dw.counts = plan.bounds ? (const int32_t *)(w + plan.off_counts) : nullptr;
     // Small batches skip the plan kernel: the decode and prefill kernels find
     // their own work, and the decode list is then every request of the batch.
     // Every prefill workgroup repeats its search over all requests, which pays
@@ -306,7 +336,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     // with the plan kernel's list).  Decode-only batches plan in the kernel up
     // to kSelfPlanReqs requests (one search per decode workgroup).
     const bool has_decode = plan.n_decode_reqs > 0, has_prefill = plan.n_prefill_items > 0;
-    const bool self_plan = p.R <= (has_prefill ? kSelfPlanPrefillReqs : kSelfPlanReqs) &&
+    const bool self_plan = !plan.bounds && p.R <= (has_prefill ? kSelfPlanPrefillReqs : kSelfPlanReqs) &&
                            env_int("RA_SELF_PLAN", 1) != 0;
     dw.self_plan = self_plan ? 1 : 0;
     if (self_plan && has_decode) dw.nd = p.R;
@@ -322,7 +352,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     // A batch with both kinds of work runs its prefill kernel beside the
     // decode kernel (not when the caller times the stages), and the decode
     // kernel then leaves part of the compute units to it at first.
-    const bool overlap = allow_overlap && !ev.events && has_decode && has_prefill &&
+    const bool overlap = allow_overlap && !plan.bounds && !ev.events && has_decode && has_prefill &&
                          env_int("RA_MIXED_OVERLAP", 1) != 0;
     if (has_decode) {
         int fill = 0, cus = 0;
@@ -357,7 +387,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
                            p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg, plan.n_prefill_items,
                            (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
-                           (int32_t *)(w + plan.off_ppfx), pre);
+                           (int32_t *)(w + plan.off_ppfx), pre, (int32_t *)dw.counts);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -369,13 +399,13 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         if (err == hipSuccess) err = hipEventRecord(ss->fork, stream);
         if (err == hipSuccess) err = launch_decode(p, dw, stream, ev);
         if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
-        if (err == hipSuccess) err = launch_prefill(p, plan, pre, self_plan, ss->s);
+        if (err == hipSuccess) err = launch_prefill(p, plan, pre, self_plan, nullptr, ss->s);
         if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
         if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
         return err;
     }
     err = ev.record(1);
-    if (err == hipSuccess && has_prefill) err = launch_prefill(p, plan, pre, self_plan, stream);
+    if (err == hipSuccess && has_prefill) err = launch_prefill(p, plan, pre, self_plan, dw.counts, stream);
     if (err == hipSuccess) err = ev.record(2);
     if (err == hipSuccess) {
         if (has_decode) {

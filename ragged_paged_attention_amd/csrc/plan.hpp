@@ -176,8 +176,17 @@ __device__ __forceinline__ void self_plan_prefill_item(const Params &p, int k, i
 // Upper bound of decode workgroups per call (all head groups together); it
 // sizes the partial-result slots of the workspace independently of the GPU.
 constexpr int kMaxDecodeWorkgroups = 512;
+// Fewest pages a decode workgroup's range holds: the grid never has more
+// workgroups per head group than decode pages / kMinDecodePages, so every
+// workgroup between the first and last of a request owns pages (and a
+// partial result the merge kernel reads).
+constexpr int kMinDecodePages = 4;
 
 struct Plan {
+    // Planning on the device from upper bounds (no host copies of the
+    // lengths): the counts below are bounds, the plan kernel always runs and
+    // writes the real counts to the workspace, and no launch depends on them.
+    bool bounds = false;
     // classification
     int n_decode_reqs = 0, n_prefill_reqs = 0;
     // decode
@@ -196,6 +205,8 @@ struct Plan {
     size_t off_dreq = 0, off_dpfx = 0, off_wstart = 0;
     size_t off_part_o = 0, off_part_ml = 0;
     size_t off_ppfx = 0, off_prefill = 0;
+    size_t off_counts = 0;      // int32 {decode requests, decode pages, prefill items, decode
+                                // workgroups per head group} (bounds mode)
     size_t workspace_bytes = 0;
 };
 
@@ -213,6 +224,9 @@ struct DecodeWork {
     int self_plan;          // 1: no plan kernel; the list is every request of the batch (nd =
                             // R, dreq unused), the decode kernel finds its own start and writes
                             // dpfx of the decode requests for the merge kernel
+    const int32_t *counts;  // planning on the device: {nd, np, prefill items, workgroups} written
+                            // by the plan kernel (nd, np and nwg above are then only bounds; the
+                            // launched workgroups past counts[3] exit), else null
 };
 
 // Optional hipEvents recorded at the stage boundaries of one call.
@@ -226,6 +240,8 @@ struct StageEvents {
     }
 };
 
+// cu_h / ctx_h: host copies of cu_q_lens and context_lens, or both null to
+// plan from the upper bounds R and T alone (bounds mode).
 void make_plan(const ra_shape &s, const int32_t *cu_h, const int32_t *ctx_h, Plan *plan);
 
 // allow_overlap: a mixed batch may run its prefill kernel on the calling
@@ -248,8 +264,10 @@ hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stre
                          const StageEvents &ev);
 // items: the plan kernel's list, or null when the kernel finds its own
 // items (self_plan_prefill_item; batches without decode requests).
+// counts: planning on the device (the item count is counts[2]; a fixed grid
+// loops over the items), else null.
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
-                          hipStream_t stream);
+                          const int32_t *counts, hipStream_t stream);
 bool prefill_supports(int D, int G);
 // Query rows (heads x tokens) of one prefill workgroup for this head_dim.
 int prefill_rows(int D);

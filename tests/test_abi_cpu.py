@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from ragged_paged_attention_amd import binding
-from ragged_paged_attention_amd.inputs import config, random_batch
+from ragged_paged_attention_amd.inputs import build_batch, config, random_batch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ragged_attn.h")
@@ -159,6 +159,28 @@ def test_any_group_size_is_accepted(lib, hq, hkv):
                      head_dim=64, decode_frac=0.5)
     assert validate(b) == "RA_OK"
     assert binding.workspace_bytes(shape_for(b), b.cu_q_lens, b.context_lens) > 0
+
+
+def test_workspace_bound_covers_every_batch_of_the_same_size(lib):
+    """Planning on the device sizes the workspace from R and T alone (host
+    copies NULL): that bound is at least the workspace of any batch with R
+    requests and T new tokens, whatever its decode/prefill mix."""
+    rng = np.random.default_rng(12)
+    for Hq, Hkv, D in ((32, 8, 128), (16, 8, 256), (8, 1, 64), (64, 2, 128)):
+        R, T = 9, 300
+        for _ in range(20):
+            cuts = np.sort(rng.integers(0, T + 1, R - 1))
+            q = np.diff(np.concatenate([[0], cuts, [T]])).tolist()
+            c = rng.integers(0, 5000, R).tolist()
+            b = build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, seed=1)
+            shape = shape_for(b)
+            exact = binding.workspace_bytes(shape, b.cu_q_lens, b.context_lens)
+            bound = binding.workspace_bytes(shape, None, None)
+            assert bound >= exact > 0
+    shape = shape_for(b)
+    cu = b.cu_q_lens.clone()
+    # one host copy without the other is refused
+    assert lib.ra_workspace_bytes(ctypes.byref(shape), ctypes.c_void_p(cu.data_ptr()), None) == 0
 
 
 def test_empty_batch_is_a_no_op(lib):

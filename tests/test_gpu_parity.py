@@ -56,6 +56,19 @@ def oracle_full(b: Batch):
                           b.slot_mapping.numpy(), scale=b.effective_scale(), causal=b.causal)
 
 
+def run_gpu_device_planned(b: Batch, variant="auto"):
+    """run_gpu without host copies of the lengths: the library plans on the device."""
+    dev = torch.device("cuda:0")
+    kc = b.k_cache.to(dev)
+    vc = b.v_cache.to(dev)
+    out = binding.forward(b.q.to(dev), b.k_new.to(dev), b.v_new.to(dev), kc, vc,
+                          b.page_table.to(dev), b.cu_q_lens.to(dev), b.context_lens.to(dev),
+                          b.slot_mapping.to(dev), causal=b.causal, scale=b.scale or None,
+                          variant=variant, plan_on_device=True)
+    torch.cuda.synchronize()
+    return out.cpu(), kc.cpu(), vc.cpu()
+
+
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     """Half a bf16 ulp at |x| (8 significant bits)."""
     e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
@@ -191,6 +204,87 @@ def test_large_groups(case, variant):
     b = random_batch(seed, num_reqs=R, max_q=mq, max_ctx=mc, num_q_heads=Hq, num_kv_heads=Hkv,
                      head_dim=D, decode_frac=frac, causal=causal)
     check_small(b, variant)
+
+
+DEVICE_PLANNED = {
+    # name: (q_lens, ctx_lens, Hq, Hkv, D, causal)
+    "decode_only": ([1] * 9, [5000, 3, 1700, 16, 31, 4096, 900, 0, 2500], 32, 8, 128, True),
+    "prefill_only": ([300, 2, 0, 129, 64, 1000], [0, 50, 7, 200, 1, 3000], 16, 8, 128, True),
+    "mixed": ([1, 40, 1, 0, 130, 1, 1, 9], [3000, 0, 17, 5, 700, 1200, 0, 90], 32, 8, 128, True),
+    "mixed_noncausal": ([1, 70, 1, 33], [900, 150, 20, 0], 16, 4, 64, False),
+    "mixed_d256": ([1, 70, 1, 1, 33], [2100, 33, 0, 600, 5], 16, 8, 256, True),
+    "group_32": ([1, 20, 1, 7], [400, 10, 33, 90], 64, 2, 128, True),
+    "many_requests": ([1 if i % 7 else 3 for i in range(700)], [(11 * i) % 300 for i in range(700)],
+                      8, 2, 64, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEVICE_PLANNED))
+def test_planning_on_the_device(name):
+    """No host copies of cu_q_lens / context_lens: grids sized from the bounds
+    R and T, every count computed by the plan kernel; same bar as always."""
+    q, c, Hq, Hkv, D, causal = DEVICE_PLANNED[name]
+    b = build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, causal=causal,
+                    seed=sum(map(ord, name)) + 7, name=f"device_planned_{name}")
+    say(f"[parity] {b.name}: R={b.num_reqs} T={b.total_tokens}")
+    out, kc, vc = run_gpu_device_planned(b)
+    ref, rkc, rvc = oracle_full(b)
+    assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc)
+    assert_close(out, ref, b.name)
+
+
+def test_graph_replays_with_changing_lengths():
+    """One call captured in a HIP graph with the lengths planned on the device,
+    then replayed for batches of the same R requests and T tokens but other
+    decode/prefill mixes and context lengths (new metadata, inputs and cache
+    copied into the captured buffers before each replay): every replay
+    matches the oracle for the batch it was given."""
+    R, T, Hq, Hkv, D = 6, 120, 16, 4, 128
+    mixes = [  # (q_lens, ctx_lens): R requests, T new tokens each time
+        ([1, 1, 1, 1, 1, 115], [900, 40, 3000, 0, 17, 0]),
+        ([60, 1, 57, 1, 0, 1], [0, 2500, 300, 1, 9, 700]),
+        ([20, 20, 20, 20, 20, 20], [0, 100, 200, 300, 400, 500]),
+        ([1, 1, 1, 1, 1, 115], [5, 6, 7, 8, 9, 3900]),
+    ]
+    P = max(sum((qq + cc + 15) // 16 for qq, cc in zip(q, c)) for q, c in mixes) + 4
+    M = max(max((qq + cc + 15) // 16 for qq, cc in zip(q, c)) for q, c in mixes)
+    batches = [build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, num_pages=P,
+                           max_pages_per_req=M, seed=900 + i, name=f"replay_{i}")
+               for i, (q, c) in enumerate(mixes)]
+    dev = torch.device("cuda:0")
+    b0 = batches[0]
+    static = [t.to(dev).clone() for t in (b0.q, b0.k_new, b0.v_new, b0.k_cache, b0.v_cache,
+                                          b0.page_table, b0.cu_q_lens, b0.context_lens,
+                                          b0.slot_mapping)]
+    out = torch.empty_like(static[0])
+    shape = binding.shape_of(static[0], static[3], static[5], static[7])
+    ws = torch.empty(max(binding.workspace_bytes(shape, None, None), 256), dtype=torch.uint8, device=dev)
+
+    def call():
+        binding.forward(*static, causal=True, out=out, workspace=ws, plan_on_device=True)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream, as for any capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(2):
+        for b in batches:
+            for dst, src in zip(static, (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
+                                         b.cu_q_lens, b.context_lens, b.slot_mapping)):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            ref, rkc, rvc = oracle_full(b)
+            assert np.array_equal(u16(static[3].cpu()), rkc), f"{b.name} replay {rep}: k_cache"
+            assert np.array_equal(u16(static[4].cpu()), rvc), f"{b.name} replay {rep}: v_cache"
+            worst = assert_close(out.cpu(), ref, f"{b.name} replay {rep}")
+            say(f"[parity] graph replay {rep} of {b.name} (q_lens {b.q_lens}): max abs error {worst:.3g}")
 
 
 def test_validate_switch_checks_device_metadata(monkeypatch):
