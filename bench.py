@@ -259,12 +259,15 @@ def cpu_baseline(b: Batch, kind: str, budget_s: float):
 
 def sweep_decode(args):
     """Decode bandwidth against context length: 128 requests x 1 new token,
-    every request at the same context c, Llama-3-8B shapes."""
+    every request at the same context c; Llama-3-8B shapes (Hq=32, Hkv=8,
+    head_dim 128) or, with --head-dim 256, Hq=16, Hkv=8, head_dim 256."""
     from ragged_paged_attention_amd.inputs import build_batch
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
+    D = args.head_dim
+    Hq = 32 if D == 128 else 16
     for c in (128, 256, 512, 1024, 2048, 4096, 8192):
-        b = build_batch([1] * 128, [c] * 128, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        b = build_batch([1] * 128, [c] * 128, num_q_heads=Hq, num_kv_heads=8, head_dim=D,
                         seed=2000 + c, name=f"decode_c{c}")
         dt = [t.to(dev) for t in (b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.page_table,
                                   b.cu_q_lens, b.context_lens, b.slot_mapping)]
@@ -288,11 +291,38 @@ def sweep_decode(args):
         for t in timers:
             t.close()
         B = algorithmic_bytes(b)
-        print(json.dumps({"sweep": "decode_context", "context": c, "requests": 128,
+        print(json.dumps({"sweep": "decode_context", "context": c, "requests": 128, "head_dim": D,
                           "step_us": us, "GB_per_s": B / us / 1e3, "frac_of_8TBs": B / us / 1e3 / HBM_PEAK_GBS,
                           "decode_kernel_us": dec_us, "kernel_GB_per_s": B / dec_us / 1e3,
                           "algorithmic_bytes": B, "tokens_per_s": 128 / (us * 1e-6)}), flush=True)
         del call, dt
+
+
+def sweep_short_chunks(args):
+    """Short prefill chunks (a few new tokens after a long context, as in
+    speculative verification or chunked-prefill tails): K/V bandwidth with
+    the chunks in the decode kernel (q G <= 16 query rows) and, with
+    RA_SHORT_CHUNKS=0, in the prefill kernel."""
+    from ragged_paged_attention_amd.inputs import build_batch
+    cases = [  # (requests, new tokens, context, Hq, Hkv, D)
+        (128, 4, 4096, 32, 8, 128), (128, 2, 4096, 32, 8, 128), (128, 16, 2048, 8, 8, 128),
+        (64, 16, 2048, 32, 8, 128), (128, 8, 2048, 16, 8, 256)]
+    for n, q, c, hq, hkv, d in cases:
+        b = build_batch([q] * n, [c] * n, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                        seed=5000 + q + c, name="short")
+        B = algorithmic_bytes(b)
+        for routed in ("1", "0"):
+            os.environ["RA_SHORT_CHUNKS"] = routed
+            us, st = time_call(b, args)
+            print(json.dumps({"sweep": "short_chunks", "requests": n, "new_tokens": q, "context": c,
+                              "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
+                              "rows_per_kv_head": q * hq // hkv,
+                              "kernel": "decode" if routed == "1" and q * hq // hkv <= 16 else "prefill",
+                              "step_us": us, "GB_per_s": B / us / 1e3,
+                              "frac_of_8TBs": B / us / 1e3 / HBM_PEAK_GBS,
+                              "kernel_us": {k: v * 1e3 for k, v in st.items()}}), flush=True)
+        os.environ.pop("RA_SHORT_CHUNKS", None)
+        del b
 
 
 def time_call(b: Batch, args):
@@ -368,9 +398,14 @@ def main():
     ap.add_argument("--sweep-decode", action="store_true",
                     help="instead of the contract line: one JSON line per decode context length "
                          "(128 requests x 1 token, context 128 .. 8192), HBM fraction against context")
+    ap.add_argument("--head-dim", type=int, default=128, choices=[128, 256],
+                    help="head_dim of --sweep-decode (128: Hq=32 Hkv=8; 256: Hq=16 Hkv=8)")
     ap.add_argument("--sweep-shapes", action="store_true",
                     help="instead of the contract line: one JSON line per head_dim x page_size "
                          "(64/128/256 x 16/32/64) for a decode batch and a causal prefill batch")
+    ap.add_argument("--sweep-short-chunks", action="store_true",
+                    help="instead of the contract line: one JSON line per short-chunk batch (a few new "
+                         "tokens after long contexts), decode-kernel routing against the prefill kernel")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run 5 device-to-device copies of this many MiB (counter calibration)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -396,6 +431,9 @@ def main():
         return
     if args.sweep_shapes:
         sweep_shapes(args)
+        return
+    if args.sweep_short_chunks:
+        sweep_short_chunks(args)
         return
 
     extras = [] if args.extra_configs in ("", "none") else args.extra_configs.split(",")

@@ -111,8 +111,9 @@ typedef enum {
  * merge counters and the partial results of decode requests that several
  * workgroups share).  Host copies of cu_q_lens [R+1] and context_lens [R]
  * are read; with both NULL the result is the bound that covers every batch
- * of the shape's R requests and T new tokens (planning on the device, see
- * ra_forward).  Returns 0 when the shape is invalid or only one host copy is
+ * of the shape's R requests and T new tokens planned on the device (see
+ * ra_forward; a batch planned from host copies may need more when short
+ * chunks run in the decode kernel).  Returns 0 when the shape is invalid or only one host copy is
  * given.  The size does not depend on the variant.
  */
 size_t ra_workspace_bytes(const ra_shape *shape, const int32_t *cu_q_lens_host,
@@ -194,7 +195,8 @@ ra_status ra_forward_profiled(const ra_shape *shape,
  * once per device, on the first call with that device current).  A batch
  * whose ra_workspace_bytes() exceeds 64 MiB is refused with RA_E_WORKSPACE
  * before anything is launched (Llama-3-8B shapes need about 17 MB whatever
- * the batch's context lengths).  The call allocates nothing itself: a batch
+ * the batch's context lengths; short chunks that would widen that past the
+ * limit in the decode kernel run in the prefill kernel instead).  The call allocates nothing itself: a batch
  * with both decode and prefill requests runs its kernels one after the other
  * on `stream`, without the side stream ra_forward may create.  All calls on
  * one device share the array and each call overwrites what the last one left

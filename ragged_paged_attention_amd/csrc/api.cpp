@@ -191,7 +191,8 @@ ra_status forward_impl(const ra_shape *s, const void *q, const void *k_new, cons
                        const int32_t *cu_q_lens, const int32_t *context_lens,
                        const int32_t *slot_mapping, const int32_t *cu_h, const int32_t *ctx_h,
                        void *out, void *workspace, size_t workspace_bytes, void *stream,
-                       int32_t variant, void *const *events, int32_t n_events, bool allow_side_stream) {
+                       int32_t variant, void *const *events, int32_t n_events, bool allow_side_stream,
+                       bool short_chunks = true) {
     g_last_error.clear();
     if (events && n_events != ra::kNumStageEvents)
         return fail(RA_E_SHAPE, "n_events must be %d", ra::kNumStageEvents);
@@ -213,7 +214,7 @@ ra_status forward_impl(const ra_shape *s, const void *q, const void *k_new, cons
         return fail(RA_E_NULL, "k_cache and v_cache are required");
 
     ra::Plan plan;
-    ra::make_plan(*s, cu_h, ctx_h, &plan);
+    ra::make_plan(*s, cu_h, ctx_h, &plan, short_chunks);
     if (workspace_bytes < plan.workspace_bytes)
         return fail(RA_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                     plan.workspace_bytes);
@@ -228,6 +229,7 @@ ra_status forward_impl(const ra_shape *s, const void *q, const void *k_new, cons
 
     ra::Params p{};
     p.prefill_only = 0;
+    p.dq_max = plan.dq_max;
     p.skip_scatter = (variant == RA_VARIANT_UNFUSED && plan.specialised_ok) ? 1 : 0;
     p.q = (const ra::bf16_t *)q;
     p.k_new = (const ra::bf16_t *)k_new;
@@ -363,6 +365,13 @@ ra_status ra_forward_noalloc(const ra_shape *s, const void *q, const void *k_new
     if (st != RA_OK) return st;
     ra::Plan plan;
     ra::make_plan(*s, cu_h, ctx_h, &plan);
+    // Short chunks in the decode kernel widen the partial slots; if that
+    // does not fit, they run in the prefill kernel instead.
+    bool short_chunks = true;
+    if (plan.workspace_bytes > kScratchBytes && plan.dq_max > 1) {
+        short_chunks = false;
+        ra::make_plan(*s, cu_h, ctx_h, &plan, false);
+    }
     if (plan.workspace_bytes > kScratchBytes)
         return fail(RA_E_WORKSPACE, "the batch needs %zu bytes of workspace; the static scratch holds %zu",
                     plan.workspace_bytes, kScratchBytes);
@@ -375,7 +384,7 @@ ra_status ra_forward_noalloc(const ra_shape *s, const void *q, const void *k_new
     // kernels one after the other on `stream`.
     return forward_impl(s, q, k_new, v_new, k_cache, v_cache, page_table, cu_q_lens, context_lens,
                         slot_mapping, cu_h, ctx_h, out, ws, kScratchBytes, stream, RA_VARIANT_AUTO,
-                        nullptr, 0, false);
+                        nullptr, 0, false, short_chunks);
 }
 
 }  // extern "C"

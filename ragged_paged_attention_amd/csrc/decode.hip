@@ -39,9 +39,14 @@
 //   * the online softmax runs on S^T: per-head max across the 4 lane groups
 //     by two cross-lane steps, running sum kept per lane and reduced once;
 //     the accumulator is rescaled only when a max grows past a headroom.
-// The workgroup that computes a request's last page writes the new token's
-// K/V rows into the cache (the fused update); attention reads that key from
-// k_new/v_new, so no workgroup reads a slot this launch writes.
+// A short prefill chunk (q new tokens with q G <= 16, as in speculative
+// verification or the tail of a chunked prefill) runs here too: its Q^T
+// columns are the q tokens x G heads (column n: token n / G, head n % G),
+// each column with its own causal limit, and its q new K/V rows are read
+// from k_new / v_new.  The workgroup that computes a page block holding new
+// tokens writes their K/V rows into the cache (the fused update); attention
+// reads those keys from k_new/v_new, so no workgroup reads a slot this
+// launch writes.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -127,8 +132,9 @@ struct DecodeTile {
 struct DecodeReq {
     int i;     // index in the decode request list
     int r;     // request id
-    int t0;    // its (single) token
-    int c;     // context length = position of the new token
+    int t0;    // its first new token
+    int q;     // new tokens (1, or a short chunk)
+    int c;     // context length = position of the first new token
     int pfx;   // first flat page
     int pend;  // one past its last flat page
 };
@@ -140,9 +146,6 @@ __device__ __forceinline__ int ld_meta(const int32_t *a, size_t i) {
     return ((const __attribute__((address_space(4))) int32_t *)a)[i];
 }
 
-// 16-row blocks of a decode request with c prior tokens (c + 1 keys).
-__device__ __forceinline__ int blocks_of(int c) { return (c + 16) >> 4; }
-
 // Decode request i of the list, whose first flat page is pfx.  Without a
 // plan kernel the list is every request of the batch, and those that are
 // not decode requests hold no pages (the walks step over them).
@@ -151,10 +154,11 @@ __device__ __forceinline__ DecodeReq make_req(const Params &p, const DecodeWork 
     q.i = i;
     q.r = dw.self_plan ? i : ld_meta(dw.dreq, i);
     q.t0 = ld_meta(p.cu_q_lens, q.r);
+    q.q = ld_meta(p.cu_q_lens, q.r + 1) - q.t0;
     q.c = ld_meta(p.context_lens, q.r);
-    const bool decode = !dw.self_plan || ld_meta(p.cu_q_lens, q.r + 1) - q.t0 == 1;
+    const bool decode = !dw.self_plan || decode_kind(q.q, p.dq_max);
     q.pfx = pfx;
-    q.pend = pfx + (decode ? blocks_of(q.c) : 0);
+    q.pend = pfx + (decode ? decode_blocks(q.c, q.q) : 0);
     return q;
 }
 
@@ -179,8 +183,8 @@ __device__ __forceinline__ int2 self_plan_first(const Params &p, const DecodeWor
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
         const int r = 64 * k + lane;
-        const bool decode = r < R && p.cu_q_lens[r + 1] - p.cu_q_lens[r] == 1;
-        nb[k] = decode ? blocks_of(p.context_lens[r]) : 0;
+        const int qn = r < R ? p.cu_q_lens[r + 1] - p.cu_q_lens[r] : 0;
+        nb[k] = decode_kind(qn, p.dq_max) ? decode_blocks(p.context_lens[r], qn) : 0;
     }
     int base = 0, first = -1, first_pfx = 0;
 #pragma unroll
@@ -218,8 +222,8 @@ __device__ __forceinline__ int2 self_plan_range(const Params &p, int x0, int x1)
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
         const int r = 64 * k + lane;
-        const bool decode = r < R && p.cu_q_lens[r + 1] - p.cu_q_lens[r] == 1;
-        nb[k] = decode ? blocks_of(p.context_lens[r]) : 0;
+        const int qn = r < R ? p.cu_q_lens[r + 1] - p.cu_q_lens[r] : 0;
+        nb[k] = decode_kind(qn, p.dq_max) ? decode_blocks(p.context_lens[r], qn) : 0;
     }
     int base = 0, at0 = 0, at1 = 0;
 #pragma unroll
@@ -367,14 +371,17 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         const bf16_t *vnew = p.v_new + (size_t)lq.t0 * Hkv * D;
 #pragma unroll
         for (int u = 0; u < NC; ++u) {
-            // Positions >= c are the new token (read from k_new / v_new: the
-            // same bits, and never the slot this launch writes) or lie past
-            // the request (their scores are masked; reading the new row keeps
-            // the stand-in V finite, so 0 * V stays 0).
-            const bool cached = real && pr * 16 + j0 + RPU * u < lq.c;
+            // Positions c .. c+q-1 are the new tokens (read from k_new /
+            // v_new: the same bits, and never the slots this launch writes);
+            // positions past the request (their scores are masked) read the
+            // last new row, which keeps the stand-in V finite, so 0 * V
+            // stays 0.
+            const int pos = pr * 16 + j0 + RPU * u;
+            const bool cached = real && pos < lq.c;
+            const size_t nrow = (size_t)min(max(pos - lq.c, 0), lq.q - 1) * Hkv * D;
             const int gofs = gofs0 + RPU * u * Hkv * D;
-            const bf16_t *ksrc = cached ? p.k_cache + pid * page_elems + gofs : knew + nofs;
-            const bf16_t *vsrc = cached ? p.v_cache + pid * page_elems + gofs : vnew + nofs;
+            const bf16_t *ksrc = cached ? p.k_cache + pid * page_elems + gofs : knew + nrow + nofs;
+            const bf16_t *vsrc = cached ? p.v_cache + pid * page_elems + gofs : vnew + nrow + nofs;
             tile.k[u] = stream_load(ksrc);
             tile.v[u] = stream_load(vsrc);
         }
@@ -394,12 +401,20 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     while (cq.pend == cq.pfx) cq = next_req(p, dw, cq);  // (a range may start at a request without pages)
     int seg_g = g0;  // first flat page of the current segment
     short8_t qb[KS];
-    // This lane's query head inside the group (16 per head block).
-    const int gq = 16 * hb + n16;
-    const bool hv = gq < G;
-    // Q^T as the B operand: lane (head n16, group kg) holds q[t0][hk*G + gq][32ks + 8kg .. +8].
+    // This lane's query column: 16 per head block; column col of a request
+    // with q new tokens is token col / G, head col % G, and exists when
+    // col < q G.  Set per request by load_q, with the column's last visible
+    // key.
+    const int col = 16 * hb + n16;
+    bool hv = false;
+    int icol = 0, gcol = 0, clim = 0;
+    // Q^T as the B operand: lane (column n16, group kg) holds q[t0 + icol][hk*G + gcol][32ks + 8kg .. +8].
     auto load_q = [&]() {
-        const bf16_t *qrow = p.q + ((size_t)cq.t0 * p.Hq + hk * G + (hv ? gq : 0)) * D;
+        hv = col < cq.q * G;
+        icol = hv ? col / G : 0;
+        gcol = hv ? col - icol * G : 0;
+        clim = p.causal ? cq.c + icol : cq.c + cq.q - 1;
+        const bf16_t *qrow = p.q + ((size_t)(cq.t0 + icol) * p.Hq + hk * G + gcol) * D;
         const short8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -428,29 +443,33 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
             const short8_t a = *reinterpret_cast<const short8_t *>(kt + n16 * D + 8 * (dc ^ (n16 & SWM)));
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], s, 0, 0, 0);
         }
-        // Online softmax; this lane holds keys pr*16 + 4kg + i of head n16,
-        // visible when <= c.
+        // Online softmax; this lane holds keys pr*16 + 4kg + i of column
+        // n16, visible up to the column's limit.
         const int jb = pr * 16 + 4 * kg;
         float sc[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = (jb + i <= cq.c) ? s[i] * sl2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) sc[i] = (jb + i <= clim) ? s[i] * sl2 : -INFINITY;
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         // Lazy rescale: the reference max m_run moves only when some head's
         // page max exceeds it by more than kLazyLog2 (P <= 2^kLazyLog2
         // otherwise).  o and l share the reference, so o / l is unchanged.
+        // A column that has seen no visible key yet (m_run = -inf: a short
+        // chunk's early token in a segment of later keys) keeps o = l = 0,
+        // and its weights are 0, not exp2(-inf + inf).
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazyLog2)) {
             const float mn = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - mn);
+            const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mn);
             l_run *= alpha;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
             m_run = mn;
         }
+        const float mref = m_run == -INFINITY ? 0.f : m_run;
         float pr4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr4[i] = fast_exp2(sc[i] - m_run);
+        for (int i = 0; i < 4; ++i) pr4[i] = fast_exp2(sc[i] - mref);
         l_run += (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
         // P as a bf16 pair hi + lo (lo = the rounding residue of hi), so the
         // PV product keeps ~16 bits of P: the MFMA work is negligible next to
@@ -490,8 +509,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         // (whole-request ranges never cut a request)
         const int b_first = dw.whole ? b : wg_of_page(cq.pfx, np, nwg);
         const int b_last = dw.whole ? b : wg_of_page(cq.pend - 1, np, nwg);
-        const int h = hk * G + gq;  // q head
-        bf16_t *orow = p.out + ((size_t)cq.t0 * p.Hq + h) * D;
+        bf16_t *orow = p.out + ((size_t)(cq.t0 + icol) * p.Hq + hk * G + gcol) * D;
         if (b_first == b_last) {
             if (hv) {
                 const float inv = 1.f / l_tot;
@@ -511,7 +529,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         // (a kernel boundary makes them visible without device-wide fences,
         // which flush the L2 of every XCD and would stall the streaming).
         if (hv) {
-            const size_t sidx = (size_t)partial_slot(hg, b, b_first, nwg) * (HW * G) + w * G + gq;
+            const size_t sidx = (size_t)partial_slot(hg, b, b_first, nwg) * (HW * dw.cw) + w * dw.cw + col;
             float *prow = dw.part_o + sidx * D;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -528,17 +546,21 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     // last page, scores/softmax/PV, and the end of the segment.
     auto step = [&](int g, int stage) {
         const int pr = g - cq.pfx;
-        if (g == cq.pend - 1 && lane < CPH && hb == 0 && !p.skip_scatter) {
-            // Fused KV-cache update of the new token (position c), this
-            // wavefront's kv head: the row is in the LDS tile already (loaded
-            // from k_new / v_new), so the copy waits on no global load.
-            const int j = cq.c & 15, dc = lane;
-            const bf16_t *kt = smem + stage * STAGE + w * HEAD + j * D + 8 * (dc ^ (j & SWM));
-            const short8_t kr = *reinterpret_cast<const short8_t *>(kt);
-            const short8_t vr = *reinterpret_cast<const short8_t *>(kt + TENSOR);
-            const size_t dst = ((size_t)ld_meta(p.slot_mapping, cq.t0) * Hkv + hk) * D + 8 * dc;
-            *reinterpret_cast<short8_t *>(p.k_cache + dst) = kr;
-            *reinterpret_cast<short8_t *>(p.v_cache + dst) = vr;
+        if (lane < CPH && hb == 0 && !p.skip_scatter) {
+            // Fused KV-cache update of the new tokens in this block
+            // (positions c .. c+q-1), this wavefront's kv head: the rows are
+            // in the LDS tile already (loaded from k_new / v_new), so the
+            // copies wait on no global load.
+            const int pos_end = min(cq.c + cq.q, pr * 16 + 16);
+            for (int pos = max(cq.c, pr * 16); pos < pos_end; ++pos) {
+                const int j = pos & 15, dc = lane;
+                const bf16_t *kt = smem + stage * STAGE + w * HEAD + j * D + 8 * (dc ^ (j & SWM));
+                const short8_t kr = *reinterpret_cast<const short8_t *>(kt);
+                const short8_t vr = *reinterpret_cast<const short8_t *>(kt + TENSOR);
+                const size_t dst = ((size_t)ld_meta(p.slot_mapping, cq.t0 + pos - cq.c) * Hkv + hk) * D + 8 * dc;
+                *reinterpret_cast<short8_t *>(p.k_cache + dst) = kr;
+                *reinterpret_cast<short8_t *>(p.v_cache + dst) = vr;
+            }
         }
         compute_page(pr, stage);
         if (g == cq.pend - 1 || g == g1 - 1) {
@@ -594,17 +616,19 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
     const int nwg = dw.counts ? ld_meta(dw.counts, 3) : dw.nwg;
     const int r = dw.self_plan ? i : ld_meta(dw.dreq, i);
     const int t0 = ld_meta(p.cu_q_lens, r);
-    if (dw.self_plan && ld_meta(p.cu_q_lens, r + 1) - t0 != 1) return;  // not a decode request
-    const int pfx = ld_meta(dw.dpfx, i), pend = pfx + blocks_of(ld_meta(p.context_lens, r));
+    const int qn = ld_meta(p.cu_q_lens, r + 1) - t0;
+    if (dw.self_plan && !decode_kind(qn, p.dq_max)) return;  // not a decode-kernel request
+    const int pfx = ld_meta(dw.dpfx, i), pend = pfx + decode_blocks(ld_meta(p.context_lens, r), qn);
     const int b_first = wg_of_page(pfx, np, nwg);
     const int b_last = wg_of_page(pend - 1, np, nwg);
     if (b_first == b_last) return;  // written by the decode kernel
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n16 = lane & 15, kg = lane >> 4;
     const int G = p.Hq / p.Hkv;
-    // Query heads n16, n16 + 16, ... of this wavefront's kv head.
-    for (int gq = n16; gq < G; gq += 16) {
-        const int hl = w * G + gq;  // q head inside the head group
+    // Query columns n16, n16 + 16, ... of this wavefront's kv head (column
+    // n: token n / G, head n % G of the request's q new tokens).
+    for (int col = n16; col < qn * G; col += 16) {
+        const int hl = w * dw.cw + col;  // column inside the head group's slot
         // One pass with a running max; the slots are read kU at a time so
         // that their loads are in flight together (a request rarely spans
         // more than two or three workgroups).
@@ -619,7 +643,7 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int bb = min(b0 + u, b_last);
-                const size_t sidx = (size_t)partial_slot(hg, bb, b_first, nwg) * (HW * G) + hl;
+                const size_t sidx = (size_t)partial_slot(hg, bb, b_first, nwg) * (HW * dw.cw) + hl;
                 ms[u] = dw.part_ml[sidx * 2];
                 ls[u] = dw.part_ml[sidx * 2 + 1];
                 const float *prow = dw.part_o + sidx * D;
@@ -629,6 +653,9 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 if (b0 + u > b_last) break;
+                // (a segment with no key visible to this column: m = -inf,
+                // l = o = 0, nothing to add)
+                if (ms[u] == -INFINITY) continue;
                 const float mn = fmaxf(M, ms[u]);
                 const float a = fast_exp2(M - mn), wgt = fast_exp2(ms[u] - mn);
                 den = den * a + wgt * ls[u];
@@ -638,7 +665,8 @@ __global__ __launch_bounds__(64 * HW) void decode_merge_kernel(Params p, DecodeW
             }
         }
         const float inv = 1.f / den;
-        bf16_t *orow = p.out + ((size_t)t0 * p.Hq + (hg * HW + w) * G + gq) * D;
+        const int icol = col / G;
+        bf16_t *orow = p.out + ((size_t)(t0 + icol) * p.Hq + (hg * HW + w) * G + col - icol * G) * D;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             uint2 wv;

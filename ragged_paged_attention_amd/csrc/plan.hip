@@ -18,17 +18,34 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *plan) {
+void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *plan, bool short_chunks) {
     Plan pl;
     const int R = s.num_reqs, Hq = s.num_q_heads, Hkv = s.num_kv_heads, D = s.head_dim;
     const int G = Hq / Hkv;
     pl.bounds = !cu || !ctx;
+    // Short chunks (2 <= q <= 16 / G new tokens) run in the decode kernel,
+    // whose Q^T columns then hold q tokens x G heads (RA_SHORT_CHUNKS=0 in
+    // the environment sends them to the prefill kernel).  Not when planning
+    // on the device: the partial slots would need 16 / G times the columns.
+    const int dq_cand = std::max(1, 16 / G);
+    if (!pl.bounds && short_chunks && dq_cand > 1) {
+        const char *env = getenv("RA_SHORT_CHUNKS");
+        const bool on = !(env && env[0] == '0');
+        for (int r = 0; r < R && on; ++r) {
+            const int q = cu[r + 1] - cu[r];
+            if (q >= 2 && q <= dq_cand) {
+                pl.dq_max = dq_cand;
+                break;
+            }
+        }
+    }
+    pl.cw = pl.dq_max * G;
     long long np = 0;
     for (int r = 0; r < R && !pl.bounds; ++r) {
         const int q = cu[r + 1] - cu[r];
-        if (q == 1) {
+        if (decode_kind(q, pl.dq_max)) {
             ++pl.n_decode_reqs;
-            const long long nb = ceil_div((long long)ctx[r] + 1, 16);  // 16-row blocks of pages
+            const long long nb = decode_blocks(ctx[r], q);  // 16-row blocks of pages
             np += nb;
             pl.max_decode_pages = (int)std::max<long long>(pl.max_decode_pages, nb);
         } else if (q > 1) {
@@ -61,9 +78,9 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     }
     for (int r = 0; r < R && !pl.bounds; ++r) {
         const int q = cu[r + 1] - cu[r];
-        if (q > 1 && pl.q_tile > 0) pl.n_prefill_items += (int)ceil_div(q, pl.q_tile) * Hkv;
-        if (q == 1) dec_bytes += (double)(ctx[r] + 1) * Hkv * D * 4;
-        if (q > 1) {
+        if (q > pl.dq_max && pl.q_tile > 0) pl.n_prefill_items += (int)ceil_div(q, pl.q_tile) * Hkv;
+        if (decode_kind(q, pl.dq_max)) dec_bytes += (double)(ctx[r] + q) * Hkv * D * 4;
+        if (q > pl.dq_max) {
             const double c = ctx[r];
             const double pairs = s.causal ? q * c + 0.5 * q * (q + 1.0) : (double)q * (c + q);
             pre_flops += pairs * s.num_q_heads * 4.0 * D;
@@ -77,13 +94,13 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
         pl.decode_share_pm = (int)(1000 * std::min(0.9, std::max(0.4, td / (td + tp))));
     }
     const int nd = pl.n_decode_reqs;
-    // Two partial slots per workgroup, (kv heads of the group) x G q heads
-    // each.  The slots and the workgroup table are sized for the larger of
+    // Two partial slots per workgroup, (kv heads of the group) x cw query
+    // columns each.  The slots and the workgroup table are sized for the larger of
     // the chosen head-group size and the long-context one, so that the
     // workspace does not depend on the context lengths.
     const int hw_long = decode_heads_per_group(D, Hkv, 0, 0);
     auto wg_cap = [&](int hw) { return std::max(1, kMaxDecodeWorkgroups / (Hkv / hw)); };
-    auto slot_heads = [&](int hw) { return (size_t)(Hkv / hw) * wg_cap(hw) * 2 * hw * G; };
+    auto slot_heads = [&](int hw) { return (size_t)(Hkv / hw) * wg_cap(hw) * 2 * hw * pl.cw; };
     const size_t part_heads = std::max(slot_heads(pl.decode_hw), slot_heads(hw_long));
     const int cap_max = std::max(wg_cap(pl.decode_hw), wg_cap(hw_long));
     size_t off = 0;
@@ -159,7 +176,7 @@ __device__ int last_le(P a, int n, int x) {
 // holds that many (the count the host planned from its copies of the same
 // metadata).
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
-    const int32_t *cu, const int32_t *ctx, int R, int S, int q_tile, int Hkv, int nwg, int max_items,
+    const int32_t *cu, const int32_t *ctx, int R, int dq_max, int q_tile, int Hkv, int nwg, int max_items,
     int32_t *dreq, int32_t *dpfx, int32_t *wstart, int32_t *ppfx, int4 *pre, int32_t *counts) {
     __shared__ int buf[3][kPlanThreads];
     __shared__ int dpfx_l[kPlanLds + 1], ppfx_l[kPlanLds + 1];  // LDS copies for the searches
@@ -170,9 +187,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         int n[3] = {0, 0, 0};
         if (r < R) {
             const int q = cu[r + 1] - cu[r];
-            if (q == 1) {
+            if (decode_kind(q, dq_max)) {
                 n[0] = 1;
-                n[1] = (ctx[r] + 1 + S - 1) / S;
+                n[1] = decode_blocks(ctx[r], q);
             } else if (q > 1 && q_tile > 0) {
                 n[2] = (q + q_tile - 1) / q_tile * Hkv;
             }
@@ -324,6 +341,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     dw.np = plan.n_decode_pages;
     dw.nwg = 0;
     dw.hw = plan.decode_hw;
+    dw.cw = plan.cw;
     // Planning on the device: the plan kernel writes the real counts here,
     // and every grid below is sized from bounds.
     dw.counts = plan.bounds ? (const int32_t *)(w + plan.off_counts) : nullptr;
@@ -385,7 +403,7 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
     }
     if (!self_plan) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
-                           p.context_lens, p.R, 16, plan.q_tile, p.Hkv, dw.nwg, plan.n_prefill_items,
+                           p.context_lens, p.R, plan.dq_max, plan.q_tile, p.Hkv, dw.nwg, plan.n_prefill_items,
                            (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
                            (int32_t *)(w + plan.off_ppfx), pre, (int32_t *)dw.counts);
         err = hipGetLastError();

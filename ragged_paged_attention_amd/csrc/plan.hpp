@@ -42,6 +42,12 @@ constexpr int kSelfPlanReqs = 512;
 // request per lane of the prefill kernel's search).
 constexpr int kSelfPlanPrefillReqs = 64;
 
+// Key blocks (16 rows) a decode-kernel request with c prior and q new tokens reads.
+__host__ __device__ inline int decode_blocks(int c, int q) { return (c + q + 15) >> 4; }
+
+// Whether a request with q new tokens runs in the decode kernel.
+__host__ __device__ inline bool decode_kind(int q, int dq_max) { return q >= 1 && q <= dq_max; }
+
 // Sum (or max) over the wavefront, the same in every lane: DPP within each
 // row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
 // row_half_mirror, row_mirror), then the four row results read as scalars.
@@ -83,7 +89,7 @@ __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k,
         const int r = 64 * j + lane;
         t0s[j] = r < R ? p.cu_q_lens[r] : 0;
         const int qr = r < R ? p.cu_q_lens[r + 1] - t0s[j] : 0;
-        q[j] = qr > 1 ? qr : 0;  // decode and empty requests have no prefill items
+        q[j] = qr > p.dq_max ? qr : 0;  // decode-kernel and empty requests have no prefill items
         c[j] = r < R ? p.context_lens[r] : 0;
         nt[j] = tiles_of(q[j]);
         if (q[j]) tmax = max(tmax, (c[j] + q[j] + key_tile - 1) / key_tile);
@@ -187,6 +193,11 @@ struct Plan {
     // lengths): the counts below are bounds, the plan kernel always runs and
     // writes the real counts to the workspace, and no launch depends on them.
     bool bounds = false;
+    // Requests with 1 <= q <= dq_max new tokens run in the decode kernel,
+    // whose 16 Q^T columns then hold q tokens x G heads (dq_max = 16 / G when
+    // the batch has such short chunks, else 1); cw: columns per kv head in
+    // the decode partial slots (dq_max G).
+    int dq_max = 1, cw = 0;
     // classification
     int n_decode_reqs = 0, n_prefill_reqs = 0;
     // decode
@@ -219,6 +230,7 @@ struct DecodeWork {
     float *part_ml;         // [nhg][nwg][2][HW*G][2] partial (m, l)
     int nd, np, nwg;        // decode requests, flat pages, workgroups per head group
     int hw;                 // kv heads per workgroup
+    int cw;                 // query columns per kv head in a partial slot
     int whole;              // 1: workgroup b takes the whole requests [b nd / nwg, (b+1) nd / nwg)
                             // of the list (short contexts, self_plan only): nothing to merge
     int self_plan;          // 1: no plan kernel; the list is every request of the batch (nd =
@@ -241,8 +253,10 @@ struct StageEvents {
 };
 
 // cu_h / ctx_h: host copies of cu_q_lens and context_lens, or both null to
-// plan from the upper bounds R and T alone (bounds mode).
-void make_plan(const ra_shape &s, const int32_t *cu_h, const int32_t *ctx_h, Plan *plan);
+// plan from the upper bounds R and T alone (bounds mode).  short_chunks:
+// short chunks may run in the decode kernel (which widens the partial slots).
+void make_plan(const ra_shape &s, const int32_t *cu_h, const int32_t *ctx_h, Plan *plan,
+               bool short_chunks = true);
 
 // allow_overlap: a mixed batch may run its prefill kernel on the calling
 // thread's side stream beside the decode kernel (otherwise the kernels run

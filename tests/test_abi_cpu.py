@@ -161,10 +161,13 @@ def test_any_group_size_is_accepted(lib, hq, hkv):
     assert binding.workspace_bytes(shape_for(b), b.cu_q_lens, b.context_lens) > 0
 
 
-def test_workspace_bound_covers_every_batch_of_the_same_size(lib):
+def test_workspace_bound_covers_every_batch_of_the_same_size(lib, monkeypatch):
     """Planning on the device sizes the workspace from R and T alone (host
-    copies NULL): that bound is at least the workspace of any batch with R
-    requests and T new tokens, whatever its decode/prefill mix."""
+    copies NULL): that bound is at least the workspace the same kernels need
+    for any batch with R requests and T new tokens, whatever its
+    decode/prefill mix (planning on the device sends short chunks to the
+    prefill kernel, as RA_SHORT_CHUNKS=0 does for host planning)."""
+    monkeypatch.setenv("RA_SHORT_CHUNKS", "0")
     rng = np.random.default_rng(12)
     for Hq, Hkv, D in ((32, 8, 128), (16, 8, 256), (8, 1, 64), (64, 2, 128)):
         R, T = 9, 300

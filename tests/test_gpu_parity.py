@@ -206,6 +206,51 @@ def test_large_groups(case, variant):
     check_small(b, variant)
 
 
+SHORT_CHUNKS = {
+    # name: (q_lens, ctx_lens, Hq, Hkv, D, causal, page_size): chunks of q new
+    # tokens with q G <= 16 run in the decode kernel (columns: q tokens x G heads)
+    "g4_q2_q3_q4": ([2, 3, 4, 1, 4], [900, 14, 30, 200, 2000], 32, 8, 128, True, 16),
+    "g4_no_context": ([3, 4, 2, 1], [0, 0, 0, 0], 16, 4, 128, True, 16),
+    "g4_block_edges": ([4, 4, 4, 4, 3], [12, 13, 14, 15, 16], 16, 4, 64, True, 16),
+    "g1_q16": ([16, 9, 1, 16], [500, 7, 40, 3000], 8, 8, 128, True, 16),
+    "g2_q8_noncausal": ([8, 5, 2, 1], [300, 77, 0, 90], 8, 4, 64, False, 16),
+    "g8_q2": ([2, 2, 1, 2], [1000, 3, 60, 17], 64, 8, 128, True, 16),
+    "g16_q2_goes_to_prefill": ([2, 1, 2], [100, 40, 0], 16, 1, 64, True, 16),
+    "d256_g2_q8": ([8, 3, 1, 6], [700, 20, 300, 0], 16, 8, 256, True, 16),
+    "with_long_chunks": ([4, 300, 1, 3, 64, 2], [4000, 0, 900, 33, 500, 1], 32, 8, 128, True, 16),
+    "page_64": ([4, 3, 2, 1], [130, 63, 64, 5], 32, 8, 128, True, 64),
+    "short_contexts_whole_ranges": ([1, 2, 1, 4, 3] * 12, [(13 * i) % 90 for i in range(60)], 32, 8, 128, True, 16),
+    "many_requests_plan_kernel": ([1 + (i % 4) for i in range(600)], [(37 * i) % 700 for i in range(600)],
+                                  16, 4, 64, True, 16),
+}
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("name", sorted(SHORT_CHUNKS))
+def test_short_chunks(name, variant):
+    q, c, Hq, Hkv, D, causal, S = SHORT_CHUNKS[name]
+    b = build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, causal=causal, page_size=S,
+                    num_pages=sum((x + y + S - 1) // S for x, y in zip(q, c)) + 2,
+                    seed=sum(map(ord, name)) + 11, name=f"short_{name}")
+    check_small(b, variant)
+
+
+def test_short_chunks_agree_with_the_prefill_kernel(monkeypatch):
+    """The same batch with short chunks in the decode kernel and (with
+    RA_SHORT_CHUNKS=0) in the prefill kernel: caches bitwise equal, outputs
+    both within the oracle's bound and within 2 x of it of each other."""
+    q, c, Hq, Hkv, D, causal, S = SHORT_CHUNKS["with_long_chunks"]
+    b = build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, seed=5150, name="short_ab")
+    o1, k1, _ = run_gpu(b)
+    monkeypatch.setenv("RA_SHORT_CHUNKS", "0")
+    o2, k2, _ = run_gpu(b)
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+    ref, _, _ = oracle_full(b)
+    assert_close(o1, ref, "short chunks in the decode kernel")
+    assert_close(o2, ref, "short chunks in the prefill kernel")
+    assert float((o1.float() - o2.float()).abs().max()) <= 2 * TOL
+
+
 DEVICE_PLANNED = {
     # name: (q_lens, ctx_lens, Hq, Hkv, D, causal)
     "decode_only": ([1] * 9, [5000, 3, 1700, 16, 31, 4096, 900, 0, 2500], 32, 8, 128, True),

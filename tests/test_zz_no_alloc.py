@@ -73,3 +73,15 @@ def test_noalloc_refuses_a_batch_beyond_the_scratch():
     assert e.value.name == "RA_E_WORKSPACE"
     torch.cuda.synchronize()
     assert bool((sentinel == 3.0).all())
+
+
+def test_noalloc_short_chunks_beyond_the_slot_limit():
+    """Short chunks at Llama-3-8B shapes would widen the decode partial slots
+    past the 64 MiB scratch; the call then runs them in the prefill kernel and
+    still matches the oracle."""
+    b = build_batch([4, 1, 3, 2] * 8, [(97 * i) % 3000 for i in range(32)], num_q_heads=32,
+                    num_kv_heads=8, head_dim=128, seed=504, name="noalloc_short")
+    out, kc, vc = _run(b, binding.forward_noalloc)
+    ref, rkc, rvc = oracle_full(b)
+    assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc)
+    assert_close(out, ref, b.name)
