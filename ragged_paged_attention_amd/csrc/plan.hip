@@ -417,13 +417,13 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         if (err == hipSuccess) err = hipEventRecord(ss->fork, stream);
         if (err == hipSuccess) err = launch_decode(p, dw, stream, ev);
         if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
-        if (err == hipSuccess) err = launch_prefill(p, plan, pre, self_plan, nullptr, ss->s);
+        if (err == hipSuccess) err = launch_prefill(p, plan, pre, self_plan, nullptr, true, ss->s);
         if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
         if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
         return err;
     }
     err = ev.record(1);
-    if (err == hipSuccess && has_prefill) err = launch_prefill(p, plan, pre, self_plan, dw.counts, stream);
+    if (err == hipSuccess && has_prefill) err = launch_prefill(p, plan, pre, self_plan, dw.counts, false, stream);
     if (err == hipSuccess) err = ev.record(2);
     if (err == hipSuccess) {
         if (has_decode) {

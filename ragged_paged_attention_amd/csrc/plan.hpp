@@ -65,18 +65,20 @@ __device__ __forceinline__ int wave_reduce_i(int x) {
 // Prefill item k of a batch of KR * 64 requests at most, found without the
 // plan kernel.  Items go out longest first: in decreasing order of the key
 // tiles (key_tile keys each) they read, ties in request order, then rank
-// (query tile from the last one back), then kv head.  The hardware starts
-// workgroups in index order as compute units free up, so this is
-// longest-processing-time-first scheduling across all requests.  Every lane
-// of the calling wavefront must take part: lane l holds requests l, l + 64,
-// ... (one round trip of loads); a binary search over the tile count, each
+// (query tile from the last one back), then kv head: with one item per
+// workgroup the hardware starts workgroups in index order as compute units
+// free up, so this is longest-processing-time-first scheduling across all
+// requests, and with one workgroup per unit looping over the items in snake
+// order the units get even sums of item lengths.  Every lane of the calling
+// wavefront must take part: lane l holds requests l, l + 64, ... (one round
+// trip of loads, from cu / ctxl); a binary search over the tile count, each
 // step a wave sum of per-request counts in closed form, finds the tile count
 // of item k, and a wave scan finds its request, whose metadata the owning
 // lane already holds.  A result that falls outside the batch (not expected)
 // turns the item into a no-op (it.x = -1).
-template <int KR>
+template <int KR, typename Ptr>
 __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k, int q_tile, int key_tile,
-                                                         int4 &it, int4 &it2) {
+                                                         int4 &it, int4 &it2, Ptr cu, Ptr ctxl) {
     const int lane = threadIdx.x & 63, R = p.R, Hkv = p.Hkv;
     // Query tiles: a shift when q_tile is a power of two (G a power of two).
     const bool pow2 = (q_tile & (q_tile - 1)) == 0;
@@ -87,10 +89,10 @@ __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k,
 #pragma unroll
     for (int j = 0; j < KR; ++j) {
         const int r = 64 * j + lane;
-        t0s[j] = r < R ? p.cu_q_lens[r] : 0;
-        const int qr = r < R ? p.cu_q_lens[r + 1] - t0s[j] : 0;
+        t0s[j] = r < R ? cu[r] : 0;
+        const int qr = r < R ? cu[r + 1] - t0s[j] : 0;
         q[j] = qr > p.dq_max ? qr : 0;  // decode-kernel and empty requests have no prefill items
-        c[j] = r < R ? p.context_lens[r] : 0;
+        c[j] = r < R ? ctxl[r] : 0;
         nt[j] = tiles_of(q[j]);
         if (q[j]) tmax = max(tmax, (c[j] + q[j] + key_tile - 1) / key_tile);
     }
@@ -172,11 +174,23 @@ __device__ __forceinline__ void self_plan_prefill_item_k(const Params &p, int k,
     it2 = make_int4(ctx, qr, 0, 0);
 }
 
-// As above for a batch of at most kSelfPlanPrefillReqs requests.
+// As above for a batch of at most kSelfPlanPrefillReqs requests, reading
+// cu_q_lens and context_lens from the device metadata.
 __device__ __forceinline__ void self_plan_prefill_item(const Params &p, int k, int q_tile, int key_tile,
                                                        int4 &it, int4 &it2) {
     static_assert(kSelfPlanPrefillReqs == 64, "one request per lane");
-    self_plan_prefill_item_k<1>(p, k, q_tile, key_tile, it, it2);
+    self_plan_prefill_item_k<1>(p, k, q_tile, key_tile, it, it2, p.cu_q_lens, p.context_lens);
+}
+
+// The same from copies in LDS (cu: R + 1 entries, ctx: R entries), which a
+// kernel that plans once per item takes at its start: vector memory
+// operations complete in issue order, so global loads here would wait for
+// every store and load the kernel has in flight.
+typedef const __attribute__((address_space(3))) int32_t *lds_i32_ptr;
+__device__ __forceinline__ void self_plan_prefill_item_lds(const Params &p, int k, int q_tile, int key_tile,
+                                                           int4 &it, int4 &it2, lds_i32_ptr cu, lds_i32_ptr ctx) {
+    static_assert(kSelfPlanPrefillReqs == 64, "one request per lane");
+    self_plan_prefill_item_k<1>(p, k, q_tile, key_tile, it, it2, cu, ctx);
 }
 
 // Upper bound of decode workgroups per call (all head groups together); it
@@ -277,11 +291,14 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
 hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream,
                          const StageEvents &ev);
 // items: the plan kernel's list, or null when the kernel finds its own
-// items (self_plan_prefill_item; batches without decode requests).
-// counts: planning on the device (the item count is counts[2]; a fixed grid
-// loops over the items), else null.
+// items (self_plan_prefill_item).
+// counts: planning on the device (the item count is counts[2], the grid is
+// sized from the bound plan.n_prefill_items), else null.
+// spread: one workgroup per item (a mixed batch's prefill kernel beside the
+// decode kernel); else, up to head_dim 128, one workgroup per compute unit
+// that loops over its items.
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
-                          const int32_t *counts, hipStream_t stream);
+                          const int32_t *counts, bool spread, hipStream_t stream);
 bool prefill_supports(int D, int G);
 // Query rows (heads x tokens) of one prefill workgroup for this head_dim.
 int prefill_rows(int D);
