@@ -301,12 +301,13 @@ def sweep_decode(args):
 def sweep_short_chunks(args):
     """Short prefill chunks (a few new tokens after a long context, as in
     speculative verification or chunked-prefill tails): K/V bandwidth with
-    the chunks in the decode kernel (q G <= 16 query rows) and, with
-    RA_SHORT_CHUNKS=0, in the prefill kernel."""
+    the chunks in the decode kernel (q G <= 32 query columns per kv head, in
+    blocks of 16) and, with RA_SHORT_CHUNKS=0, in the prefill kernel."""
     from ragged_paged_attention_amd.inputs import build_batch
     cases = [  # (requests, new tokens, context, Hq, Hkv, D)
         (128, 4, 4096, 32, 8, 128), (128, 2, 4096, 32, 8, 128), (128, 16, 2048, 8, 8, 128),
-        (64, 16, 2048, 32, 8, 128), (128, 8, 2048, 16, 8, 256)]
+        (128, 8, 2048, 32, 8, 128), (64, 16, 2048, 32, 8, 128), (64, 32, 2048, 16, 8, 128),
+        (128, 8, 2048, 16, 8, 256)]
     for n, q, c, hq, hkv, d in cases:
         b = build_batch([q] * n, [c] * n, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
                         seed=5000 + q + c, name="short")
@@ -317,7 +318,8 @@ def sweep_short_chunks(args):
             print(json.dumps({"sweep": "short_chunks", "requests": n, "new_tokens": q, "context": c,
                               "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                               "rows_per_kv_head": q * hq // hkv,
-                              "kernel": "decode" if routed == "1" and q * hq // hkv <= 16 else "prefill",
+                              "kernel": "decode" if routed == "1" and q * hq // hkv <= 32 else "prefill",
+                              "column_blocks": (q * hq // hkv + 15) // 16 if routed == "1" and q * hq // hkv <= 32 else 0,
                               "step_us": us, "GB_per_s": B / us / 1e3,
                               "frac_of_8TBs": B / us / 1e3 / HBM_PEAK_GBS,
                               "kernel_us": {k: v * 1e3 for k, v in st.items()}}), flush=True)

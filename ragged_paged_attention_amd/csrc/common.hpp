@@ -25,7 +25,7 @@ struct Params {
     int32_t prefill_only;   // generic kernel: skip tokens of decode (q_r == 1) requests
     int32_t skip_scatter;   // attention kernels leave the cache alone (a separate scatter ran)
     int32_t dq_max;         // requests with 1 <= q_r <= dq_max run in the decode kernel (one
-                            // decode token, or a short chunk of q_r G <= 16 query rows)
+                            // decode token, or a short chunk of q_r G <= 32 query columns)
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

@@ -18,8 +18,8 @@
 // every K/V byte its wavefront reads (grouped-query attention), so the cache
 // is read exactly once when G <= 16.  Larger groups are cut into blocks of 16
 // query heads on the grid's third dimension: each block's workgroups stream
-// the same pages (the cache is then read ceil(G / 16) times).  Per 16-token
-// page:
+// the same pages, at the same time and on the same XCD, so that the blocks
+// after the first mostly find them in L2.  Per 16-token page:
 //   * the workgroup loads the page's K and V blocks of its HW heads with
 //     16-byte loads in address order (each token row holds the HW heads
 //     side by side, so a page arrives as 16 contiguous segments of up to
@@ -39,9 +39,10 @@
 //   * the online softmax runs on S^T: per-head max across the 4 lane groups
 //     by two cross-lane steps, running sum kept per lane and reduced once;
 //     the accumulator is rescaled only when a max grows past a headroom.
-// A short prefill chunk (q new tokens with q G <= 16, as in speculative
+// A short prefill chunk (q new tokens with q G <= 32, as in speculative
 // verification or the tail of a chunked prefill) runs here too: its Q^T
-// columns are the q tokens x G heads (column n: token n / G, head n % G),
+// columns are the q tokens x G heads (column n: token n / G, head n % G;
+// blocks of 16 columns on the grid's third dimension, like head blocks),
 // each column with its own causal limit, and its q new K/V rows are read
 // from k_new / v_new.  The workgroup that computes a page block holding new
 // tokens writes their K/V rows into the cache (the fused update); attention
@@ -91,13 +92,13 @@ __device__ __forceinline__ short4_t lds_read_tr16(const bf16_t *p) {
 #define RA_DECODE_NT 1
 #endif
 
+// NT: non-temporal loads (off where several column slices of the grid read
+// the same pages and should find them in L2).
+template <bool NT>
 __device__ __forceinline__ short8_t stream_load(const bf16_t *src) {
     const short8_t *p = reinterpret_cast<const short8_t *>(src);
-#if RA_DECODE_NT
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
+    if constexpr (NT && RA_DECODE_NT) return __builtin_nontemporal_load(p);
+    else return *p;
 }
 
 // Page ids a decode workgroup stages in LDS at a time.
@@ -257,7 +258,7 @@ __device__ __forceinline__ int partial_slot(int hg, int b, int b_first, int nwg)
     return (hg * nwg + b) * 2 + (b == b_first ? 1 : 0);
 }
 
-template <int D, int HW, int PF>
+template <int D, int HW, int PF, bool NT>
 __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw) {
     using C = DecodeCfg<D, HW>;
     constexpr int KS = C::KS, MB = C::MB, CPH = C::CPH, CPR = C::CPR, NTHR = C::NTHR,
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n16 = lane & 15, kg = lane >> 4;
-    const int hg = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;  // hb: block of 16 query heads
+    const int hg = blockIdx.x, b = blockIdx.y, hb = blockIdx.z;  // hb: block of 16 query columns
     // (planning on the device: the page and workgroup counts the plan
     // kernel wrote; the launched workgroups past them have nothing to do)
     const int np = dw.counts ? ld_meta(dw.counts, 1) : dw.np;
@@ -382,8 +383,8 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
             const int gofs = gofs0 + RPU * u * Hkv * D;
             const bf16_t *ksrc = cached ? p.k_cache + pid * page_elems + gofs : knew + nrow + nofs;
             const bf16_t *vsrc = cached ? p.v_cache + pid * page_elems + gofs : vnew + nrow + nofs;
-            tile.k[u] = stream_load(ksrc);
-            tile.v[u] = stream_load(vsrc);
+            tile.k[u] = stream_load<NT>(ksrc);
+            tile.v[u] = stream_load<NT>(vsrc);
         }
     };
     auto store_page = [&](int stage, const DecodeTile<NC> &tile) {
@@ -681,9 +682,12 @@ template <int D, int HW, int PF>
 hipError_t configure_decode() {
     static bool configured = false;
     if (!configured) {
-        hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<D, HW, PF>,
+        hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<D, HW, PF, true>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)DecodeCfg<D, HW>::LDS_BYTES);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void *)decode_kernel<D, HW, PF, false>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)DecodeCfg<D, HW>::LDS_BYTES);
         if (e != hipSuccess) return e;
         configured = true;
     }
@@ -699,7 +703,7 @@ hipError_t decode_capacity(int *cap) {
     e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, HW, PF>, 64 * HW,
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<D, HW, PF, true>, 64 * HW,
                                                          DecodeCfg<D, HW>::LDS_BYTES);
     if (e != hipSuccess) return e;
     *cap = std::max(1, cus * std::max(1, per_cu));
@@ -711,9 +715,17 @@ hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t 
                              const StageEvents &ev) {
     hipError_t e = configure_decode<D, HW, PF>();
     if (e != hipSuccess) return e;
-    const dim3 grid(p.Hkv / HW, dw.nwg, (p.Hq / p.Hkv + 15) / 16);
+    // One slice of the grid per 16 query columns of a kv head (G heads, or
+    // q tokens x G heads of a short chunk); the slices of one page range
+    // (same x, y) are 8k workgroups apart, on one XCD, and resident together,
+    // so they read each page from HBM about once and from L2 otherwise.
+    const int slices = decode_column_blocks(dw.cw);
+    const dim3 grid(p.Hkv / HW, dw.nwg, slices);
     const size_t lds = DecodeCfg<D, HW>::LDS_BYTES;
-    hipLaunchKernelGGL((decode_kernel<D, HW, PF>), grid, dim3(64 * HW), lds, stream, p, dw);
+    if (slices == 1)
+        hipLaunchKernelGGL((decode_kernel<D, HW, PF, true>), grid, dim3(64 * HW), lds, stream, p, dw);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, HW, PF, false>), grid, dim3(64 * HW), lds, stream, p, dw);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = ev.record(3);
@@ -796,9 +808,10 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
     // RA_DECODE_WGS (environment) overrides the resident count, for tuning.
     const char *env = getenv("RA_DECODE_WGS");
     const int forced = env ? atoi(env) : 0;
-    // Groups of more than 16 query heads launch one grid slice per block of
-    // 16 heads: together they fill the resident slots once.
-    const int hblocks = (p.Hq / p.Hkv + 15) / 16;
+    // More than 16 query columns per kv head (groups of more than 16 heads,
+    // or wide short chunks) launch one grid slice per block of 16 columns:
+    // together they fill the resident slots once.
+    const int hblocks = decode_column_blocks(plan.cw);
     if (forced > 0) cap = forced * plan.decode_hgroups * hblocks;
     int n = std::max(1, cap / (plan.decode_hgroups * hblocks));
     if (fill) *fill = n;  // workgroups per head group that fill every compute unit once
@@ -806,6 +819,9 @@ hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *
     // (planning on the device: the page count is unknown here; workgroups
     // whose range is empty exit at once)
     if (!plan.bounds) n = std::min(n, whole > 0 ? whole : std::max(1, plan.n_decode_pages / kMinDecodePages));
+    // With several slices, a multiple of 8 workgroups per slice keeps the
+    // slices of one page range on one XCD (workgroups go to XCDs round robin).
+    if (hblocks > 1 && n >= 8) n -= n % 8;
     *nwg = n;
     return hipSuccess;
 }

@@ -23,20 +23,38 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
     const int R = s.num_reqs, Hq = s.num_q_heads, Hkv = s.num_kv_heads, D = s.head_dim;
     const int G = Hq / Hkv;
     pl.bounds = !cu || !ctx;
-    // Short chunks (2 <= q <= 16 / G new tokens) run in the decode kernel,
-    // whose Q^T columns then hold q tokens x G heads (RA_SHORT_CHUNKS=0 in
-    // the environment sends them to the prefill kernel).  Not when planning
-    // on the device: the partial slots would need 16 / G times the columns.
-    const int dq_cand = std::max(1, 16 / G);
-    if (!pl.bounds && short_chunks && dq_cand > 1) {
+    // Short chunks (2 <= q new tokens, q G <= kShortColumns query columns)
+    // run in the decode kernel, whose Q^T columns then hold q tokens x G heads
+    // in blocks of 16 (one grid slice each).  dq_max is the largest q of the
+    // smallest block count (1 or 2) that takes every such chunk of the batch;
+    // more than one block is used only when those wider chunks hold at least
+    // half of the decode kernel's pages (the extra slices also stream the
+    // pages of every other decode request, for no column); otherwise the
+    // wider chunks go to the prefill kernel.  RA_SHORT_CHUNKS=0 in the
+    // environment sends all chunks to the prefill kernel.  Not when planning
+    // on the device: the partial slots would need the wider column count.
+    if (!pl.bounds && short_chunks && G <= kShortColumns / 2) {
         const char *env = getenv("RA_SHORT_CHUNKS");
         const bool on = !(env && env[0] == '0');
+        int qmax = 0;
         for (int r = 0; r < R && on; ++r) {
             const int q = cu[r + 1] - cu[r];
-            if (q >= 2 && q <= dq_cand) {
-                pl.dq_max = dq_cand;
-                break;
+            if (q >= 2 && q * G <= kShortColumns) qmax = std::max(qmax, q);
+        }
+        const int dq1 = 16 / G;  // one block
+        if (qmax > 0 && qmax <= dq1) {
+            pl.dq_max = dq1;
+        } else if (qmax > 0) {
+            const int dq = kShortColumns / G;
+            long long wide = 0, all = 0;
+            for (int r = 0; r < R; ++r) {
+                const int q = cu[r + 1] - cu[r];
+                if (q < 1 || q > dq) continue;
+                const long long nb = decode_blocks(ctx[r], q);
+                all += nb;
+                if (q > dq1) wide += nb;
             }
+            pl.dq_max = 2 * wide >= all ? dq : std::max(1, dq1);
         }
     }
     pl.cw = pl.dq_max * G;

@@ -48,6 +48,15 @@ __host__ __device__ inline int decode_blocks(int c, int q) { return (c + q + 15)
 // Whether a request with q new tokens runs in the decode kernel.
 __host__ __device__ inline bool decode_kind(int q, int dq_max) { return q >= 1 && q <= dq_max; }
 
+// Query columns per kv head a short chunk may bring to the decode kernel
+// (q tokens x G heads), and the 16-column blocks (grid slices) of cw columns.
+// Every slice runs the whole page pipeline, and a decode workgroup is bound
+// by its page rate, not by HBM: two slices beat the prefill kernel on such
+// chunks (128 x 8 tokens after 2048, G = 4: 3.77 against 3.44 TB/s), four
+// did not (64 x 16: 2.19 against 3.22 TB/s).
+constexpr int kShortColumns = 32;
+__host__ __device__ inline int decode_column_blocks(int cw) { return (cw + 15) / 16; }
+
 // Sum (or max) over the wavefront, the same in every lane: DPP within each
 // row of 16 lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
 // row_half_mirror, row_mirror), then the four row results read as scalars.

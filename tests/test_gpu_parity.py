@@ -208,14 +208,24 @@ def test_large_groups(case, variant):
 
 SHORT_CHUNKS = {
     # name: (q_lens, ctx_lens, Hq, Hkv, D, causal, page_size): chunks of q new
-    # tokens with q G <= 16 run in the decode kernel (columns: q tokens x G heads)
+    # tokens with q G <= 32 run in the decode kernel (columns: q tokens x G
+    # heads, in blocks of 16), two blocks only where the chunks that need them
+    # hold at least half of the decode kernel's pages
     "g4_q2_q3_q4": ([2, 3, 4, 1, 4], [900, 14, 30, 200, 2000], 32, 8, 128, True, 16),
     "g4_no_context": ([3, 4, 2, 1], [0, 0, 0, 0], 16, 4, 128, True, 16),
     "g4_block_edges": ([4, 4, 4, 4, 3], [12, 13, 14, 15, 16], 16, 4, 64, True, 16),
     "g1_q16": ([16, 9, 1, 16], [500, 7, 40, 3000], 8, 8, 128, True, 16),
     "g2_q8_noncausal": ([8, 5, 2, 1], [300, 77, 0, 90], 8, 4, 64, False, 16),
     "g8_q2": ([2, 2, 1, 2], [1000, 3, 60, 17], 64, 8, 128, True, 16),
-    "g16_q2_goes_to_prefill": ([2, 1, 2], [100, 40, 0], 16, 1, 64, True, 16),
+    "g16_q2_two_blocks": ([2, 1, 2], [100, 40, 0], 16, 1, 64, True, 16),
+    "g16_q2_goes_to_prefill": ([2, 1, 1], [10, 3000, 2000], 16, 1, 64, True, 16),
+    "g4_q16_goes_to_prefill": ([16, 12, 9, 16], [2048, 100, 7, 500], 32, 8, 128, True, 16),
+    "g4_q8_two_blocks": ([8, 6, 5, 1], [700, 33, 0, 90], 32, 8, 128, True, 16),
+    "g4_mixed_widths": ([8, 3, 1, 7, 2, 16], [1500, 40, 200, 900, 16, 0], 16, 4, 64, True, 16),
+    "g4_wide_but_few_pages": ([8, 1, 1, 1], [20, 3000, 2500, 4000], 32, 8, 128, True, 16),
+    "g2_q16_noncausal": ([16, 9, 1, 12], [100, 0, 60, 333], 8, 4, 128, False, 16),
+    "d256_g2_q16": ([16, 10, 1, 15], [300, 40, 50, 1000], 16, 8, 256, True, 16),
+    "g32_q2_goes_to_prefill": ([2, 2, 1], [500, 70, 30], 64, 2, 64, True, 16),
     "d256_g2_q8": ([8, 3, 1, 6], [700, 20, 300, 0], 16, 8, 256, True, 16),
     "with_long_chunks": ([4, 300, 1, 3, 64, 2], [4000, 0, 900, 33, 500, 1], 32, 8, 128, True, 16),
     "page_64": ([4, 3, 2, 1], [130, 63, 64, 5], 32, 8, 128, True, 64),
@@ -235,11 +245,12 @@ def test_short_chunks(name, variant):
     check_small(b, variant)
 
 
-def test_short_chunks_agree_with_the_prefill_kernel(monkeypatch):
+@pytest.mark.parametrize("name", ["with_long_chunks", "g4_q8_two_blocks"])
+def test_short_chunks_agree_with_the_prefill_kernel(name, monkeypatch):
     """The same batch with short chunks in the decode kernel and (with
     RA_SHORT_CHUNKS=0) in the prefill kernel: caches bitwise equal, outputs
     both within the oracle's bound and within 2 x of it of each other."""
-    q, c, Hq, Hkv, D, causal, S = SHORT_CHUNKS["with_long_chunks"]
+    q, c, Hq, Hkv, D, causal, S = SHORT_CHUNKS[name]
     b = build_batch(q, c, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, seed=5150, name="short_ab")
     o1, k1, _ = run_gpu(b)
     monkeypatch.setenv("RA_SHORT_CHUNKS", "0")
