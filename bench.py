@@ -355,6 +355,28 @@ def time_call(b: Batch, args):
     return us, stages
 
 
+def sweep_prefill_length(args):
+    """Prefill throughput against chunk length at a fixed 16384 new tokens per
+    call: 16384 / L requests of L tokens, no context, causal and non-causal;
+    Llama-3-8B shapes (Hq=32, Hkv=8, head_dim 128).  Short chunks pay the
+    per-item start and end and the partial diagonal tiles; long ones converge
+    to the key-tile loop's rate."""
+    from ragged_paged_attention_amd.inputs import build_batch
+    for causal in (True, False):
+        for L in (128, 256, 512, 1024, 2048, 4096, 8192, 16384):
+            n = 16384 // L
+            b = build_batch([L] * n, [0] * n, num_q_heads=32, num_kv_heads=8, head_dim=128, causal=causal,
+                            seed=6000 + L, name="prefill_len")
+            us, st = time_call(b, args)
+            F = algorithmic_flops(b)
+            print(json.dumps({"sweep": "prefill_length", "causal": causal, "chunk_tokens": L, "requests": n,
+                              "step_us": us, "TFLOP_per_s": F / us / 1e6,
+                              "frac_of_peak": F / us / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+                              "prefill_kernel_us": st["prefill"],
+                              "kernel_TFLOP_per_s": F / st["prefill"] / 1e6}), flush=True)
+            del b
+
+
 def sweep_shapes(args):
     """head_dim x page_size: a decode batch (128 requests x 1 token, context
     4096) and a causal prefill batch (4 x 2048 tokens), Hkv = 8, G = 4 at
@@ -409,6 +431,8 @@ def main():
     ap.add_argument("--sweep-shapes", action="store_true",
                     help="instead of the contract line: one JSON line per head_dim x page_size "
                          "(64/128/256 x 16/32/64) for a decode batch and a causal prefill batch")
+    ap.add_argument("--sweep-prefill-length", action="store_true",
+                    help="prefill TFLOP/s against chunk length (16384 new tokens per call)")
     ap.add_argument("--sweep-short-chunks", action="store_true",
                     help="instead of the contract line: one JSON line per short-chunk batch (a few new "
                          "tokens after long contexts), decode-kernel routing against the prefill kernel")
@@ -440,6 +464,9 @@ def main():
         return
     if args.sweep_short_chunks:
         sweep_short_chunks(args)
+        return
+    if args.sweep_prefill_length:
+        sweep_prefill_length(args)
         return
 
     extras = [] if args.extra_configs in ("", "none") else args.extra_configs.split(",")
