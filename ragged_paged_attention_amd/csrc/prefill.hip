@@ -45,6 +45,8 @@
 // The workgroup copies the new K/V rows of its item's tokens into the cache
 // (each (token, kv head) row is written exactly once), and writes the output
 // rows through LDS up to head_dim 128 so that every store covers whole rows.
+#include <stdlib.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -952,6 +954,12 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
+        // RA_PREFILL_WGS (environment) caps the looping grid, for tuning and
+        // for tests of many rounds per workgroup.
+        if (const char *env = getenv("RA_PREFILL_WGS")) {
+            const int forced = atoi(env);
+            if (forced > 0) cus = std::min(cus, forced);
+        }
         hipLaunchKernelGGL((prefill_pp_kernel<D, D <= 128>), dim3(std::min(std::max(1, cus), n)),
                            dim3(PingPongCfg<D>::NTHR), 0, stream, p, items, self_plan ? 1 : 0, plan.q_tile, counts,
                            plan.n_prefill_items);

@@ -289,6 +289,27 @@ def test_planning_on_the_device(name):
     assert_close(out, ref, b.name)
 
 
+@pytest.mark.parametrize("self_plan", ["1", "0"])
+def test_prefill_item_loop_many_rounds(self_plan, monkeypatch):
+    """The looping prefill kernel with its grid capped at 3 workgroups (80
+    rounds each: past the 64 rounds whose items the kernel lists in LDS at
+    its start it finds each item at the item's start), self-planned and from
+    the plan kernel's list: caches bitwise equal to the oracle's, outputs
+    within its bound and bitwise equal to the full grid's."""
+    q = [130, 64, 300, 77, 450, 129, 90, 250, 33, 9]  # prefill only (every chunk wider than 8 G columns)
+    c = [0, 40, 0, 500, 10, 0, 64, 1000, 7, 3]
+    b = build_batch(q, c, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=8080, name="item_loop_rounds")
+    monkeypatch.setenv("RA_SELF_PLAN", self_plan)
+    full, _, _ = run_gpu(b)
+    monkeypatch.setenv("RA_PREFILL_WGS", "3")
+    say(f"[parity] item_loop_rounds self_plan={self_plan} RA_PREFILL_WGS=3")
+    out, kc, vc = run_gpu(b)
+    ref, rkc, rvc = oracle_full(b)
+    assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc), "caches differ from the oracle's"
+    assert_close(out, ref, b.name)
+    assert torch.equal(out.view(torch.int16), full.view(torch.int16)), "grid size changed the output"
+
+
 def test_graph_replays_with_changing_lengths():
     """One call captured in a HIP graph with the lengths planned on the device,
     then replayed for batches of the same R requests and T tokens but other
