@@ -257,6 +257,22 @@ def cpu_baseline(b: Batch, kind: str, budget_s: float):
             "tokens_per_s": toks / secs, "seconds": secs}
 
 
+def warm_up(call, stream, n: int, min_ms: float = 40.0):
+    """n untimed calls, then more until at least min_ms have passed: the
+    part's clock settles over tens of milliseconds of back-to-back work, which
+    a fixed count of short calls (50 calls of a 20-60 us batch) does not
+    cover, so a sweep point measured right after a change of batch read up to
+    14 % slow."""
+    t0 = time.perf_counter()
+    for _ in range(n):
+        call(stream)
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(10):
+            call(stream)
+        torch.cuda.synchronize()
+
+
 def sweep_decode(args):
     """Decode bandwidth against context length: 128 requests x 1 new token,
     every request at the same context c; Llama-3-8B shapes (Hq=32, Hkv=8,
@@ -273,8 +289,7 @@ def sweep_decode(args):
                                   b.cu_q_lens, b.context_lens, b.slot_mapping)]
         call = binding.Prepared(*dt, causal=True, scale=None, variant=args.variant,
                                 cu_q_lens_host=b.cu_q_lens, context_lens_host=b.context_lens)
-        for _ in range(args.warmup):
-            call(stream)
+        warm_up(call, stream, args.warmup)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -335,8 +350,7 @@ def time_call(b: Batch, args):
                               b.cu_q_lens, b.context_lens, b.slot_mapping)]
     call = binding.Prepared(*dt, causal=b.causal, scale=None, variant=args.variant,
                             cu_q_lens_host=b.cu_q_lens, context_lens_host=b.context_lens)
-    for _ in range(args.warmup):
-        call(stream)
+    warm_up(call, stream, args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
