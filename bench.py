@@ -423,11 +423,14 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # Fifty untimed calls: over its first ~30 back-to-back calls after the
-    # process starts GPU work the part's clock swings (the head_dim-256 decode
-    # kernel from 425 to 549 us and back to ~440, causal prefill 167 -> 215 ->
-    # ~170 us); the timed calls then see the steady rate.
-    ap.add_argument("--warmup", type=int, default=50)
+    # 400 untimed calls per workload: the part's clock settles over tens of
+    # milliseconds of back-to-back work, after the process starts GPU work
+    # (the head_dim-256 decode kernel from 425 to 549 us and back to ~440)
+    # and again when the work changes from HBM-bound decode to MFMA-bound
+    # prefill.  Fifty calls (8 ms of causal prefill) left the prefill lines
+    # 3-8 % slow (168.4 against 155.0 us per step, same box); 400 cost well
+    # under a second in all.
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--config", default="decode", choices=[c for c in CONFIGS])
     ap.add_argument("--variant", default="auto", choices=list(binding.VARIANTS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
