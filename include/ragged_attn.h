@@ -44,17 +44,19 @@
  * L_r < 2^30 (key positions are 32-bit inside the kernels).
  *
  * Ownership and concurrency: the caller owns every buffer, the workspace
- * included; the library allocates no device memory and keeps no data
- * between calls.  Host pointers are read during the call only.  ra_forward
- * is asynchronous on `stream` (a hipStream_t; NULL is the null stream) and
- * never synchronises.  A batch with both decode and prefill requests runs
- * its prefill kernel on a second stream beside the decode kernel, forked
- * from and joined back into `stream` with events (capturable in a graph);
- * that stream and its two events are created per calling thread and device
- * on first use and live until the process ends (so one thread's graph
- * capture never absorbs another thread's eager calls).  `out` must not alias any input.  A slot written by
- * this call must not be read, as prior context, by any request of the same
- * call.  Two calls that share a workspace must be ordered on one stream.
+ * included; ra_forward allocates no device memory and keeps no data
+ * between calls (ra_forward_noalloc, below, uses a static device array
+ * instead of the workspace).  Host pointers are read during the call only.
+ * ra_forward is asynchronous on `stream` (a hipStream_t; NULL is the null
+ * stream) and never synchronises.  A batch with both decode and prefill
+ * requests runs its prefill kernel on a second stream beside the decode
+ * kernel, forked from and joined back into `stream` with events (capturable
+ * in a graph); that stream and its two events are created per calling
+ * thread and device on first use and live until the process ends (so one
+ * thread's graph capture never absorbs another thread's eager calls).
+ * `out` must not alias any input.  A slot written by this call must not be
+ * read, as prior context, by any request of the same call.  Two calls that
+ * share a workspace must be ordered on one stream.
  *
  * Errors: every entry point returns a status and never aborts; the detail of
  * the last failure on the calling thread is in ra_last_error().

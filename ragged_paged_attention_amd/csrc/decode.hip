@@ -400,7 +400,6 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     // ---- compute cursor: the request being accumulated ---------------------
     DecodeReq cq = lq;
     while (cq.pend == cq.pfx) cq = next_req(p, dw, cq);  // (a range may start at a request without pages)
-    int seg_g = g0;  // first flat page of the current segment
     short8_t qb[KS];
     // This lane's query column: 16 per head block; column col of a request
     // with q new tokens is token col / G, head col % G, and exists when
@@ -504,7 +503,7 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
     // End of a segment (the part of request cq inside this workgroup): write
     // the output when the segment is the whole request, otherwise a partial;
     // the last workgroup of the request to finish merges the partials.
-    auto finish_segment = [&](int g_last) {
+    auto finish_segment = [&]() {
         float l_tot = l_run + __shfl_xor(l_run, 16, 64);
         l_tot += __shfl_xor(l_tot, 32, 64);
         // (whole-request ranges never cut a request)
@@ -540,7 +539,6 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
                 dw.part_ml[sidx * 2 + 1] = l_tot;
             }
         }
-        (void)g_last;
     };
 
     // One flat page through the pipeline: fused KV update on the request's
@@ -565,12 +563,11 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
         }
         compute_page(pr, stage);
         if (g == cq.pend - 1 || g == g1 - 1) {
-            finish_segment(g);
+            finish_segment();
             if (g + 1 < g1) {
                 // (requests without pages hold no flat page: skip them)
                 do cq = next_req(p, dw, cq);
                 while (cq.pend == cq.pfx);
-                seg_g = g + 1;
                 load_q();
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) o[mb] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -598,7 +595,6 @@ __global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw
             step(g + k, (g + k) & 1);
         }
     }
-    (void)seg_g;
 }
 
 // Log-sum-exp merge of the partials of every decode request that several
