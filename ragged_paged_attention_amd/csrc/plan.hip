@@ -94,9 +94,15 @@ void make_plan(const ra_shape &s, const int32_t *cu, const int32_t *ctx, Plan *p
         const long long tiles = (T + pl.q_tile - 1) / pl.q_tile + std::min<long long>(R, T / 2);
         pl.n_prefill_items = (int)std::min<long long>(tiles * Hkv, 1LL << 30);
     }
+    int q_first = -1, c_first = -1;
+    pl.uniform_prefill = !pl.bounds;
     for (int r = 0; r < R && !pl.bounds; ++r) {
         const int q = cu[r + 1] - cu[r];
         if (q > pl.dq_max && pl.q_tile > 0) pl.n_prefill_items += (int)ceil_div(q, pl.q_tile) * Hkv;
+        if (q > pl.dq_max) {
+            if (q_first < 0) q_first = q, c_first = ctx[r];
+            else if (q != q_first || ctx[r] != c_first) pl.uniform_prefill = false;
+        }
         if (decode_kind(q, pl.dq_max)) dec_bytes += (double)(ctx[r] + q) * Hkv * D * 4;
         if (q > pl.dq_max) {
             const double c = ctx[r];

@@ -232,6 +232,7 @@ struct Plan {
     // prefill
     int q_tile = 0;             // query tokens per prefill work item
     int n_prefill_items = 0;    // (request, kv head, query tile) triples
+    bool uniform_prefill = false; // every prefill chunk has the same length and context
     int decode_share_pm = 1000; // mixed batches: per mille of the decode grid launched beside prefill
     // which path runs
     bool specialised_ok = false;

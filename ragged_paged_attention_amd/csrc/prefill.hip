@@ -948,8 +948,21 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
     // One workgroup per compute unit (LDS holds one), looping over the items,
     // up to head_dim 128 unless spread; else one workgroup per item (with
     // planning on the device, per bound item: those past the count exit).
+    // The loop's items are dealt out in a fixed order, which balances when
+    // the list is longest first (self-planned) or every chunk has the same
+    // shape; the plan kernel's list of ragged chunks is in request order, and
+    // there one workgroup per item, which the hardware starts as compute units
+    // free up, balances better (100 x 512-token chunks after 0-8K tokens of
+    // context: 4.29 ms looping, 4.09 ms one per workgroup; uniform batches
+    // gain 4-27 % from the loop, e.g. 128 x 256 tokens 292 -> 230 us).
+    // RA_PREFILL_LOOP=0 / 1 (environment) overrides the choice, for tests.
     const int n = std::max(1, plan.n_prefill_items);
-    if (D <= 128 && !spread) {
+    bool loop = D <= 128 && !spread && (self_plan || plan.bounds || plan.uniform_prefill);
+    if (const char *env = getenv("RA_PREFILL_LOOP")) {
+        if (env[0] == '0') loop = false;
+        else if (env[0] == '1') loop = D <= 128 && !spread;
+    }
+    if (loop) {
         int dev = 0, cus = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

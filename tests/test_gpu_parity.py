@@ -300,6 +300,9 @@ def test_prefill_item_loop_many_rounds(self_plan, monkeypatch):
     c = [0, 40, 0, 500, 10, 0, 64, 1000, 7, 3]
     b = build_batch(q, c, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=8080, name="item_loop_rounds")
     monkeypatch.setenv("RA_SELF_PLAN", self_plan)
+    # (the plan kernel's list of ragged chunks would otherwise run one item
+    # per workgroup)
+    monkeypatch.setenv("RA_PREFILL_LOOP", "1")
     full, _, _ = run_gpu(b)
     monkeypatch.setenv("RA_PREFILL_WGS", "3")
     say(f"[parity] item_loop_rounds self_plan={self_plan} RA_PREFILL_WGS=3")
@@ -308,6 +311,27 @@ def test_prefill_item_loop_many_rounds(self_plan, monkeypatch):
     assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc), "caches differ from the oracle's"
     assert_close(out, ref, b.name)
     assert torch.equal(out.view(torch.int16), full.view(torch.int16)), "grid size changed the output"
+
+
+def test_ragged_plan_list_runs_one_item_per_workgroup(monkeypatch):
+    """A prefill-only batch of more than 64 ragged chunks (the plan kernel's
+    list, in request order) runs one prefill item per workgroup; forcing the
+    looping kernel on the same list gives the same bits, and both match the
+    oracle (caches bitwise, outputs within the bound)."""
+    rng = np.random.default_rng(4242)
+    q = [int(x) for x in rng.integers(2, 200, 70)]
+    c = [int(x) for x in rng.integers(0, 600, 70)]
+    b = build_batch(q, c, num_q_heads=16, num_kv_heads=4, head_dim=128, seed=4243, name="ragged_plan_list")
+    say("[parity] ragged_plan_list default (one item per workgroup)")
+    one, kc, vc = run_gpu(b)
+    ref, rkc, rvc = oracle_full(b)
+    assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc), "caches differ from the oracle's"
+    assert_close(one, ref, b.name)
+    monkeypatch.setenv("RA_PREFILL_LOOP", "1")
+    say("[parity] ragged_plan_list RA_PREFILL_LOOP=1")
+    loop, kc2, vc2 = run_gpu(b)
+    assert np.array_equal(u16(kc2), rkc) and np.array_equal(u16(vc2), rvc), "caches differ from the oracle's"
+    assert torch.equal(loop.view(torch.int16), one.view(torch.int16)), "looping kernel changed the output"
 
 
 def test_graph_replays_with_changing_lengths():
