@@ -334,6 +334,30 @@ def test_ragged_plan_list_runs_one_item_per_workgroup(monkeypatch):
     assert torch.equal(loop.view(torch.int16), one.view(torch.int16)), "looping kernel changed the output"
 
 
+def test_uniform_batch_request_order(monkeypatch):
+    """A self-planned batch of prefill chunks of one length and context runs
+    its items in request order (closed form); longest first
+    (RA_PREFILL_ORDER=0) and a grid capped at 3 workgroups (past the 64 rounds
+    the kernel lists in LDS) give the same bits, and all match the oracle."""
+    b = build_batch([300] * 24, [100] * 24, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=5151,
+                    name="uniform_request_order")
+    say("[parity] uniform_request_order default (request order)")
+    out, kc, vc = run_gpu(b)
+    ref, rkc, rvc = oracle_full(b)
+    assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc), "caches differ from the oracle's"
+    assert_close(out, ref, b.name)
+    monkeypatch.setenv("RA_PREFILL_WGS", "3")
+    say("[parity] uniform_request_order RA_PREFILL_WGS=3")
+    capped, kc2, vc2 = run_gpu(b)
+    assert np.array_equal(u16(kc2), rkc) and np.array_equal(u16(vc2), rvc), "caches differ from the oracle's"
+    assert torch.equal(capped.view(torch.int16), out.view(torch.int16)), "grid size changed the output"
+    monkeypatch.delenv("RA_PREFILL_WGS")
+    monkeypatch.setenv("RA_PREFILL_ORDER", "0")
+    say("[parity] uniform_request_order RA_PREFILL_ORDER=0 (longest first)")
+    lf, _, _ = run_gpu(b)
+    assert torch.equal(lf.view(torch.int16), out.view(torch.int16)), "item order changed the output"
+
+
 def test_graph_replays_with_changing_lengths():
     """One call captured in a HIP graph with the lengths planned on the device,
     then replayed for batches of the same R requests and T tokens but other
