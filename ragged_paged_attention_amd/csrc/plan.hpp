@@ -14,7 +14,9 @@
 //
 // Prefill: chunks are cut into query tiles of `q_tile` tokens per kv head.
 // Self-planned batches hand the items out longest first across requests
-// (self_plan_prefill_item); the plan kernel writes them request by request.
+// (self_plan_prefill_item), or, when every request is a prefill chunk of the
+// same length and context and the kernel loops over its items, in request
+// order; the plan kernel writes them request by request.
 //
 // The host computes counts and the workspace layout only.  Decode-only
 // batches of at most kSelfPlanReqs requests, and batches with prefill chunks

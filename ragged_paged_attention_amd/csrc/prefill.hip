@@ -168,8 +168,11 @@ struct PingPongCfg {
 // device, else n_items).  With one workgroup per compute unit the rounds go
 // out in a snake order (round i from the first workgroup up when i is even,
 // from the last one down when odd), which keeps the sum of item lengths per
-// workgroup even when the items come longest first; a grid of one workgroup
-// per item (rounds = 1) leaves the balancing to the hardware's dispatch.
+// workgroup even when the items come longest first, or in request order when
+// every request has the same shape (self_plan 2); a grid of one workgroup per
+// item (rounds = 1) leaves the balancing to the hardware's dispatch.
+// self_plan: 0 items from the list, 1 found by the kernel longest first, 2 in
+// request order in closed form (prefill-only batches of one chunk shape).
 // While one item's key tiles run, the workgroup reads its next item;
 // between two items it issues the next item's first loads (Q rows, first two
 // key tiles) right behind the current item's output stores.
@@ -977,7 +980,7 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
     // shape; the plan kernel's list of ragged chunks is in request order, and
     // there one workgroup per item, which the hardware starts as compute units
     // free up, balances better (100 x 512-token chunks after 0-8K tokens of
-    // context: 4.29 ms looping, 4.09 ms one per workgroup; uniform batches
+    // context: 4.31 ms looping, 4.14 ms one per workgroup; uniform batches
     // gain 4-27 % from the loop, e.g. 128 x 256 tokens 292 -> 230 us).
     // RA_PREFILL_LOOP=0 / 1 (environment) overrides the choice, for tests.
     const int n = std::max(1, plan.n_prefill_items);
