@@ -169,10 +169,11 @@ struct PingPongCfg {
 // out in a snake order (round i from the first workgroup up when i is even,
 // from the last one down when odd), which keeps the sum of item lengths per
 // workgroup even when the items come longest first, or in request order when
-// every request has the same shape (self_plan 2); a grid of one workgroup per
+// every request has the same shape; a grid of one workgroup per
 // item (rounds = 1) leaves the balancing to the hardware's dispatch.
-// self_plan: 0 items from the list, 1 found by the kernel longest first, 2 in
-// request order in closed form (prefill-only batches of one chunk shape).
+// self_plan: 0 items from the list, 1 found by the kernel longest first,
+// 2 | rg << 8 in closed form for prefill-only batches of one chunk shape:
+// requests in groups of rg, each group longest first (rg = 1: request order).
 // While one item's key tiles run, the workgroup reads its next item;
 // between two items it issues the next item's first loads (Q rows, first two
 // key tiles) right behind the current item's output stores.
@@ -242,12 +243,14 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
     const int nb = gridDim.x, b = blockIdx.x;
     auto item_at = [&](int i) { return (i & 1) ? (i + 1) * nb - 1 - b : i * nb + b; };
     auto fetch = [&](int k, int4 &it, int4 &it2) {
-        if (self_plan == 2) {
+        if ((self_plan & 0xff) == 2) {
             // Every request a prefill chunk of the same length q and context
-            // c: request order in closed form, the same order as the plan
-            // kernel's list (a request's last query tile first, kv heads
-            // within a tile), so the items that run together read the K/V of
-            // a few requests and share L2.
+            // c: requests in groups of rg (self_plan >> 8), each group's items
+            // longest first (a request's last query tile first, then request,
+            // then kv head), in closed form.  With rg = 1 this is request
+            // order, the plan kernel's; the items that run together read the
+            // K/V of a few requests and share L2.
+            const int rg = max(1, self_plan >> 8);
             int qr, cx;
             if constexpr (LMETA) {
                 qr = __builtin_amdgcn_readfirstlane(lmeta[1] - lmeta[0]);
@@ -257,9 +260,11 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
                 cx = ld_meta(p.context_lens, 0);
             }
             const int ntiles = (qr + q_tile - 1) / q_tile, per = ntiles * p.Hkv;
-            const int r = k / per, local = k - r * per;
-            const int rank = local / p.Hkv, hk = local - rank * p.Hkv;
-            if (r >= p.R || qr <= 1) {
+            const int g = k / (rg * per), kk = k - g * rg * per;
+            const int gs = min(rg, p.R - g * rg);  // requests in group g
+            const int rank = kk / max(1, gs * p.Hkv), rem = kk - rank * gs * p.Hkv;
+            const int r = g * rg + rem / p.Hkv, hk = rem % p.Hkv;
+            if (gs < 1 || r >= p.R || qr <= 1) {
                 it = make_int4(-1, 0, 0, 0);
                 it2 = make_int4(0, 0, 0, 0);
             } else {
@@ -989,24 +994,27 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
         if (env[0] == '0') loop = false;
         else if (env[0] == '1') loop = D <= 128 && !spread;
     }
-    // Self-planned item order: longest first (1), or, for the loop over a
-    // batch whose requests are all prefill chunks of one length and context,
-    // request order (2): the items that run together then share the K/V of a
-    // few requests in L2 (same box, 64 x 1024 tokens 859 -> 777 us, 32 x 512
-    // 155 -> 145 us, 64 x 256 after 1024 tokens 407 -> 365 us; 4 x 2048 within
-    // 1 %).  One item per workgroup keeps longest first, which the
-    // hardware's hand-out of workgroups needs (head_dim 256, 4 x 2048: 177
-    // against 231 us).
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    // Self-planned item order: longest first (1), or, when every request is a
+    // prefill chunk of one length and context, requests in groups of rg, each
+    // group longest first (2 | rg << 8): the items that run together then
+    // share the K/V of a few requests in L2.  The loop takes rg = 1 (request
+    // order; same box, 64 x 1024 tokens 859 -> 777 us, 32 x 512 155 -> 145
+    // us, 64 x 256 after 1024 tokens 407 -> 365 us; 4 x 2048 within 1 %).
+    // One item per workgroup needs longest first for the hardware's hand-out
+    // of workgroups to balance (head_dim 256, 4 x 2048 in request order: 231
+    // against 177 us), so there rg is the requests whose items fill the
+    // compute units once, and each group is handed out longest first.
     // RA_PREFILL_ORDER=0 (environment) keeps longest first, for tests.
     const char *order_env = getenv("RA_PREFILL_ORDER");
     const bool uniform_all = plan.uniform_prefill && plan.n_prefill_reqs == p.R && plan.n_decode_reqs == 0 &&
-                             !(order_env && order_env[0] == '0');
-    const int mode = !self_plan ? 0 : (loop && uniform_all) ? 2 : 1;
+                             p.R > 0 && !(order_env && order_env[0] == '0');
+    const int rg = loop ? 1 : std::max(1, cus / std::max(1, plan.n_prefill_items / std::max(1, p.R)));
+    const int mode = !self_plan ? 0 : uniform_all ? (2 | (std::min(rg, 1 << 20) << 8)) : 1;
     if (loop) {
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
         // RA_PREFILL_WGS (environment) caps the looping grid, for tuning and
         // for tests of many rounds per workgroup.
         if (const char *env = getenv("RA_PREFILL_WGS")) {

@@ -334,13 +334,18 @@ def test_ragged_plan_list_runs_one_item_per_workgroup(monkeypatch):
     assert torch.equal(loop.view(torch.int16), one.view(torch.int16)), "looping kernel changed the output"
 
 
-def test_uniform_batch_request_order(monkeypatch):
+@pytest.mark.parametrize("head_dim", [128, 256])
+def test_uniform_batch_request_order(head_dim, monkeypatch):
     """A self-planned batch of prefill chunks of one length and context runs
-    its items in request order (closed form); longest first
-    (RA_PREFILL_ORDER=0) and a grid capped at 3 workgroups (past the 64 rounds
-    the kernel lists in LDS) give the same bits, and all match the oracle."""
-    b = build_batch([300] * 24, [100] * 24, num_q_heads=32, num_kv_heads=8, head_dim=128, seed=5151,
-                    name="uniform_request_order")
+    its items in request order (head_dim 128, the item loop) or in groups of
+    requests that fill the compute units once, each group longest first
+    (head_dim 256, one item per workgroup: groups of 10, 10 and 4 requests
+    here); longest first over the whole batch (RA_PREFILL_ORDER=0) and, at
+    128, a grid capped at 3 workgroups (past the 64 rounds the kernel lists in
+    LDS) give the same bits, and all match the oracle."""
+    hq = 32 if head_dim == 128 else 16
+    b = build_batch([300] * 24, [100] * 24, num_q_heads=hq, num_kv_heads=8, head_dim=head_dim, seed=5151,
+                    name=f"uniform_request_order_d{head_dim}")
     say("[parity] uniform_request_order default (request order)")
     out, kc, vc = run_gpu(b)
     ref, rkc, rvc = oracle_full(b)
