@@ -42,6 +42,8 @@ from ragged_paged_attention_amd.inputs import Batch, CONFIGS, config  # noqa: E4
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense bf16
+# Least untimed time per workload before its timed calls (after --warmup calls).
+WARMUP_MIN_MS = 100.0
 
 WORKLOADS = {
     "tiny": "tiny mixed batch: 2 decode (context 37, 100) + prefill 20 (context 0) + 33 (context 50), Hq=4 Hkv=2 D=64",
@@ -257,20 +259,24 @@ def cpu_baseline(b: Batch, kind: str, budget_s: float):
             "tokens_per_s": toks / secs, "seconds": secs}
 
 
-def warm_up(call, stream, n: int, min_ms: float = 40.0):
+def warm_up(call, stream, n: int, min_ms: float = 40.0) -> int:
     """n untimed calls, then more until at least min_ms have passed: the
     part's clock settles over tens of milliseconds of back-to-back work, which
     a fixed count of short calls (50 calls of a 20-60 us batch) does not
     cover, so a sweep point measured right after a change of batch read up to
-    14 % slow."""
+    14 % slow.  Returns the number of untimed calls made."""
     t0 = time.perf_counter()
+    done = 0
     for _ in range(n):
         call(stream)
+    done += n
     torch.cuda.synchronize()
     while (time.perf_counter() - t0) * 1e3 < min_ms:
         for _ in range(10):
             call(stream)
+        done += 10
         torch.cuda.synchronize()
+    return done
 
 
 def sweep_decode(args):
@@ -525,9 +531,11 @@ def measure(name: str, args, cpu_budget: float, per_call: bool) -> dict:
     stream = torch.cuda.current_stream(dev).cuda_stream
     log(f"[bench] {name}: R={b.num_reqs} T={b.total_tokens} pages={b.num_pages} "
         f"workspace={call.workspace.numel()} B; warmup {args.warmup}")
-    for _ in range(args.warmup):
-        call(stream)
-    torch.cuda.synchronize()
+    # --warmup untimed calls, then more until WARMUP_MIN_MS have passed on this
+    # workload: the clock settles over tens of milliseconds whenever the work
+    # changes between HBM-bound decode and MFMA-bound prefill, so a handful of
+    # untimed calls left the prefill lines several per cent slow.
+    warm_calls = warm_up(call, stream, args.warmup, WARMUP_MIN_MS)
 
     # Timed region: exactly K plain calls between events on the call's stream.
     start = torch.cuda.Event(enable_timing=True)
@@ -626,6 +634,7 @@ def measure(name: str, args, cpu_budget: float, per_call: bool) -> dict:
                       "head_dim": b.head_dim, "page_size": b.page_size, "causal": b.causal,
                       "variant": args.variant},
            "tokens_per_s": T / step_s, "frac_of_peak_whole_step": frac_step,
+           "untimed_calls": warm_calls,
            "algorithmic_bytes": B, "algorithmic_flops": F,
            "kernel_us": {k: v * 1e3 for k, v in stages.items()},
            "step_us_single_calls": pctl(single)}
