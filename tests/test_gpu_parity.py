@@ -146,6 +146,52 @@ def test_random_batches(case, variant):
     check_small(b, variant)
 
 
+# A bounded randomised sweep inside the suite: 256 batches over ten head
+# shapes, three page sizes and three kinds of batch (decode-heavy mixes with
+# long contexts, prefill chunks with or without context, many short chunks
+# after long contexts), causal and not, drawn from one master seed.  Each is
+# compared in full with the oracle (caches bitwise, output within the bound).
+SWEEP_SHAPES = [  # (Hq, Hkv, D)
+    (32, 8, 128), (16, 8, 256), (8, 2, 64), (16, 4, 128), (8, 8, 128),
+    (16, 1, 64), (12, 4, 128), (40, 8, 128), (64, 2, 64), (16, 16, 64),
+]
+
+
+def sweep_case(i: int) -> Batch:
+    rng = np.random.default_rng(777_000 + i)
+    hq, hkv, d = SWEEP_SHAPES[i % len(SWEEP_SHAPES)]
+    kind = ("mix", "prefill", "short")[(i // len(SWEEP_SHAPES)) % 3]
+    page = int(rng.choice([16, 32, 64]))
+    causal = bool(rng.random() < 0.8)
+    seed = int(rng.integers(1, 1 << 30))
+    if kind == "mix":
+        kw = dict(num_reqs=int(rng.integers(3, 9)), max_q=90, max_ctx=1200, decode_frac=0.5)
+    elif kind == "prefill":
+        kw = dict(num_reqs=int(rng.integers(1, 5)), max_q=300, max_ctx=int(rng.choice([0, 400])),
+                  decode_frac=0.0)
+    else:
+        kw = dict(num_reqs=int(rng.integers(4, 13)), max_q=6, max_ctx=1500, decode_frac=0.3)
+    b = random_batch(seed, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=page, causal=causal, **kw)
+    b.name = f"sweep{i}-{kind}-S{page}-{'causal' if causal else 'full'}"
+    return b
+
+
+@pytest.mark.parametrize("block", range(32))
+def test_randomised_sweep(block):
+    """Every fourth batch also runs planned on the device (no host copies)."""
+    worst = 0.0
+    for i in range(8 * block, 8 * block + 8):
+        b = sweep_case(i)
+        worst = max(worst, check_small(b, "auto"))
+        if i % 4 == 0:
+            say(f"[parity] {b.name} planned on the device")
+            out, kc, vc = run_gpu_device_planned(b)
+            ref, rkc, rvc = oracle_full(b)
+            assert np.array_equal(u16(kc), rkc) and np.array_equal(u16(vc), rvc), "caches differ from the oracle's"
+            worst = max(worst, assert_close(out, ref, b.name + " (device-planned)"))
+    say(f"[parity] sweep block {block}: max abs error {worst:.3g}")
+
+
 # Unit-normal batches of prefill chunks without prior context, found by a CPU
 # search (a model of the rounding of a one-bf16 P in the PV product, checked
 # against the oracle) over random batches in the space of the suite's random
