@@ -434,7 +434,7 @@ def main():
     # (the head_dim-256 decode kernel from 425 to 549 us and back to ~440)
     # and again when the work changes from HBM-bound decode to MFMA-bound
     # prefill.  Fifty calls (8 ms of causal prefill) left the prefill lines
-    # 3-8 % slow (168.4 against 155.0 us per step, same box); 400 cost well
+    # 3-8 % slow (168.4 against 155.0 us per step, same machine); 400 cost well
     # under a second in all.
     ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--config", default="decode", choices=[c for c in CONFIGS])
@@ -469,7 +469,7 @@ def main():
         ingest_counters(args)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

@@ -1002,7 +1002,7 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
     // prefill chunk of one length and context, requests in groups of rg, each
     // group longest first (2 | rg << 8): the items that run together then
     // share the K/V of a few requests in L2.  The loop takes rg = 1 (request
-    // order; same box, 64 x 1024 tokens 859 -> 777 us, 32 x 512 155 -> 145
+    // order; same machine, 64 x 1024 tokens 859 -> 777 us, 32 x 512 155 -> 145
     // us, 64 x 256 after 1024 tokens 407 -> 365 us; 4 x 2048 within 1 %).
     // One item per workgroup needs longest first for the hardware's hand-out
     // of workgroups to balance (head_dim 256, 4 x 2048 in request order: 231
