@@ -548,10 +548,10 @@ def measure(name: str, args, cpu_budget: float, per_call: bool) -> dict:
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / args.steps
 
-    # Per-kernel durations: K more calls that record hipEvents at the kernel
-    # boundaries on the same stream (the events cost a few us each, so these
-    # calls are not the ones `value` is timed on; a mixed batch runs its
-    # kernels one after the other in them, so each is timed alone).
+    # Per-kernel durations: K more calls whose kernels each carry a start and
+    # a stop hipEvent in their launch (recorded at the kernel's own start and
+    # end); these calls are not the ones `value` is timed on (a mixed batch
+    # runs its kernels one after the other in them, so each is timed alone).
     timers = [binding.StageTimer() for _ in range(args.steps)]
     for k in range(args.steps):
         call(stream, timers[k])

@@ -168,16 +168,19 @@ ra_status ra_forward_variant(const ra_shape *shape,
                              int32_t variant);
 
 /*
- * ra_forward_variant that also records caller-created hipEvent_t handles on
- * `stream` at the kernel boundaries of the call, so that the caller can time
- * each kernel: events[0] before the first launch, then events[1..4] after
- * the plan kernel, the prefill kernel, the decode kernel and the decode
- * merge kernel, in that order (a kernel that does not run still has its
- * event recorded, so its duration reads as ~0 -- the plan kernel runs only
- * for decode-only batches of more than 512 requests and batches with
- * prefill chunks of more than 64; the generic variant runs as the prefill
- * kernel).  n_events must be 5; events are not created,
- * synchronised or destroyed by the library.
+ * ra_forward_variant that also times each kernel of the call with
+ * caller-created hipEvent_t handles: events[2 s] and events[2 s + 1] are the
+ * start and stop of stage s = 0 plan kernel, 1 prefill kernel, 2 decode
+ * kernel, 3 decode merge kernel.  Each pair is given to that kernel's launch
+ * (hipExtLaunchKernel), so it brackets the kernel's execution alone, without
+ * the launch gap before it; a stage whose kernel does not run has its pair
+ * recorded back to back on `stream`, so its duration reads as ~0 (the plan
+ * kernel runs only for decode-only batches of more than 512 requests and
+ * batches with prefill chunks of more than 64; the unfused variant's scatter
+ * kernel is timed with the plan stage; the generic variant runs as the
+ * prefill kernel).  A batch with both decode and prefill requests runs its
+ * kernels one after the other in a profiled call.  n_events must be 8;
+ * events are not created, synchronised or destroyed by the library.
  */
 ra_status ra_forward_profiled(const ra_shape *shape,
                               const void *q, const void *k_new, const void *v_new,

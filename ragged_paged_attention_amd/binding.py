@@ -203,7 +203,11 @@ STAGES = ("plan", "prefill", "decode", "merge")
 
 
 class StageTimer:
-    """Five hipEvents recorded by ra_forward_profiled at the kernel boundaries."""
+    """Eight hipEvents for ra_forward_profiled: a start and a stop event per
+    stage, given to the stage's kernel launch, so that each pair brackets
+    that kernel's execution alone (a stage that launches nothing reads ~0)."""
+
+    N_EVENTS = 2 * len(STAGES)
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
@@ -212,27 +216,28 @@ class StageTimer:
                                                  ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.events = (ctypes.c_void_p * 5)()
-        for k in range(5):
+        self.events = (ctypes.c_void_p * self.N_EVENTS)()
+        for k in range(self.N_EVENTS):
             ev = ctypes.c_void_p()
             if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.events[k] = ev
 
     def stage_ms(self) -> dict:
-        """Milliseconds of each stage of the last profiled call (waits for it)."""
-        if self.hip.hipEventSynchronize(self.events[4]) != 0:
-            raise RuntimeError("hipEventSynchronize failed")
+        """Milliseconds of each stage's kernel in the last profiled call (waits for it)."""
+        for k in range(self.N_EVENTS):
+            if self.hip.hipEventSynchronize(self.events[k]) != 0:
+                raise RuntimeError("hipEventSynchronize failed")
         out = {}
         for k, name in enumerate(STAGES):
             ms = ctypes.c_float()
-            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[k], self.events[k + 1]) != 0:
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * k], self.events[2 * k + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
             out[name] = float(ms.value)
         return out
 
     def close(self):
-        for k in range(5):
+        for k in range(self.N_EVENTS):
             if self.events[k]:
                 self.hip.hipEventDestroy(self.events[k])
                 self.events[k] = None
@@ -267,6 +272,6 @@ class Prepared:
             st = self.lib.ra_forward_variant(*self.args, ctypes.c_void_p(stream), self.variant)
         else:
             st = self.lib.ra_forward_profiled(*self.args, ctypes.c_void_p(stream), self.variant,
-                                              timer.events, 5)
+                                              timer.events, StageTimer.N_EVENTS)
         _check(st)
         return self.out

@@ -258,10 +258,10 @@ ra_status forward_impl(const ra_shape *s, const void *q, const void *k_new, cons
     const char *what = "";
     if (variant == RA_VARIANT_GENERIC || !plan.specialised_ok) {
         what = "generic kernel";
-        err = ev.record(0);
-        if (err == hipSuccess) err = ev.record(1);
-        if (err == hipSuccess) err = ra::launch_generic(p, hs);
-        for (int k = 2; k < ra::kNumStageEvents && err == hipSuccess; ++k) err = ev.record(k);
+        err = ev.empty(ra::kStagePlan);
+        if (err == hipSuccess) err = ra::launch_generic(p, hs, ev.start(ra::kStagePrefill), ev.stop(ra::kStagePrefill));
+        if (err == hipSuccess) err = ev.empty(ra::kStageDecode);
+        if (err == hipSuccess) err = ev.empty(ra::kStageMerge);
     } else {
         what = "specialised kernels";
         err = ra::launch_plan(p, plan, workspace, hs, ev, allow_side_stream);

@@ -720,18 +720,15 @@ hipError_t launch_decode_cfg(const Params &p, const DecodeWork &dw, hipStream_t 
     const int slices = decode_column_blocks(dw.cw);
     const dim3 grid(p.Hkv / HW, dw.nwg, slices);
     const size_t lds = DecodeCfg<D, HW>::LDS_BYTES;
-    if (slices == 1)
-        hipLaunchKernelGGL((decode_kernel<D, HW, PF, true>), grid, dim3(64 * HW), lds, stream, p, dw);
-    else
-        hipLaunchKernelGGL((decode_kernel<D, HW, PF, false>), grid, dim3(64 * HW), lds, stream, p, dw);
-    e = hipGetLastError();
+    e = launch_kernel(slices == 1 ? decode_kernel<D, HW, PF, true> : decode_kernel<D, HW, PF, false>, grid,
+                      dim3(64 * HW), (uint32_t)lds, stream, ev.start(kStageDecode), ev.stop(kStageDecode), p, dw);
+    if (e == hipSuccess) e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = ev.record(3);
-    if (e != hipSuccess) return e;
-    if (dw.whole) return hipSuccess;  // no request is cut: nothing to merge
+    if (dw.whole) return ev.empty(kStageMerge);  // no request is cut: nothing to merge
     const dim3 mgrid(dw.nd, p.Hkv);
-    hipLaunchKernelGGL((decode_merge_kernel<D, HW>), mgrid, dim3(64), 0, stream, p, dw);
-    return hipGetLastError();
+    e = launch_kernel(decode_merge_kernel<D, HW>, mgrid, dim3(64), 0, stream, ev.start(kStageMerge),
+                      ev.stop(kStageMerge), p, dw);
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 // Calls f.template operator()<HW>() with the compile-time head-group size.

@@ -150,11 +150,14 @@ __global__ __launch_bounds__(64) void generic_kernel(Params p) {
 
 }  // namespace
 
-hipError_t launch_generic(const Params &p, hipStream_t stream) {
-    if (p.T == 0) return hipSuccess;
+hipError_t launch_generic(const Params &p, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+    if (p.T == 0) {
+        hipError_t e = ev_start ? hipEventRecord(ev_start, stream) : hipSuccess;
+        return (e == hipSuccess && ev_stop) ? hipEventRecord(ev_stop, stream) : e;
+    }
     dim3 grid(p.T, p.Hkv, (p.Hq / p.Hkv + kMaxG - 1) / kMaxG);
-    hipLaunchKernelGGL(generic_kernel, grid, dim3(64), 0, stream, p);
-    return hipGetLastError();
+    hipError_t e = launch_kernel(generic_kernel, grid, dim3(64), 0, stream, ev_start, ev_stop, p);
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 bool generic_supports(int D) { return D % 8 == 0 && D <= kMaxD; }

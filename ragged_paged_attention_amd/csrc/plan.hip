@@ -414,23 +414,29 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         if (dw.nwg > plan.decode_wg_cap) return hipErrorInvalidValue;
     }
     int4 *pre = (int4 *)(w + plan.off_prefill);
-    err = ev.record(0);
-    if (err != hipSuccess) return err;
+    // Stage kStagePlan: the unfused ablation's scatter kernel and the plan
+    // kernel, whichever run (the first launch takes the start event, the
+    // last the stop event).
+    if (!p.skip_scatter && self_plan) {
+        err = ev.empty(kStagePlan);
+        if (err != hipSuccess) return err;
+    }
     if (p.skip_scatter) {
-        // Unfused ablation: the cache update runs first as its own kernel
-        // (timed with the plan kernel in the stage events).
+        // Unfused ablation: the cache update runs first as its own kernel.
         const long long chunks = (long long)p.T * p.Hkv * (p.D / 8);
         const int blocks = (int)std::min<long long>((chunks + 255) / 256, 4096);
-        hipLaunchKernelGGL(scatter_kernel, dim3(blocks), dim3(256), 0, stream, p);
-        err = hipGetLastError();
+        err = launch_kernel(scatter_kernel, dim3(blocks), dim3(256), 0, stream, ev.start(kStagePlan),
+                            self_plan ? ev.stop(kStagePlan) : nullptr, p);
+        if (err == hipSuccess) err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     if (!self_plan) {
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.cu_q_lens,
-                           p.context_lens, p.R, plan.dq_max, plan.q_tile, p.Hkv, dw.nwg, plan.n_prefill_items,
-                           (int32_t *)dw.dreq, (int32_t *)dw.dpfx, (int32_t *)dw.wstart,
-                           (int32_t *)(w + plan.off_ppfx), pre, (int32_t *)dw.counts);
-        err = hipGetLastError();
+        err = launch_kernel(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
+                            p.skip_scatter ? nullptr : ev.start(kStagePlan), ev.stop(kStagePlan),
+                            p.cu_q_lens, p.context_lens, p.R, plan.dq_max, plan.q_tile, p.Hkv, dw.nwg,
+                            plan.n_prefill_items, (int32_t *)dw.dreq, (int32_t *)dw.dpfx,
+                            (int32_t *)dw.wstart, (int32_t *)(w + plan.off_ppfx), pre, (int32_t *)dw.counts);
+        if (err == hipSuccess) err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     if (overlap) {
@@ -446,17 +452,19 @@ hipError_t launch_plan(const Params &p, const Plan &plan, void *workspace, hipSt
         if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
         return err;
     }
-    err = ev.record(1);
-    if (err == hipSuccess && has_prefill) err = launch_prefill(p, plan, pre, self_plan, dw.counts, false, stream);
-    if (err == hipSuccess) err = ev.record(2);
+    if (has_prefill)
+        err = launch_prefill(p, plan, pre, self_plan, dw.counts, false, stream, ev.start(kStagePrefill),
+                             ev.stop(kStagePrefill));
+    else
+        err = ev.empty(kStagePrefill);
     if (err == hipSuccess) {
         if (has_decode) {
-            err = launch_decode(p, dw, stream, ev);  // records event 3 between its kernels
+            err = launch_decode(p, dw, stream, ev);  // stages kStageDecode and kStageMerge
         } else {
-            err = ev.record(3);
+            err = ev.empty(kStageDecode);
+            if (err == hipSuccess) err = ev.empty(kStageMerge);
         }
     }
-    if (err == hipSuccess) err = ev.record(4);
     return err;
 }
 

@@ -268,13 +268,22 @@ struct DecodeWork {
 };
 
 // Optional hipEvents recorded at the stage boundaries of one call.
-constexpr int kNumStageEvents = 5;
+// Profiled calls: a start and a stop event per stage (plan, prefill, decode,
+// merge), given to the stage's kernel launch itself (hipExtLaunchKernel),
+// so that each pair brackets the kernel's execution alone; a stage that
+// launches nothing has its pair recorded back to back.
+constexpr int kNumStages = 4, kNumStageEvents = 2 * kNumStages;
+enum Stage { kStagePlan = 0, kStagePrefill = 1, kStageDecode = 2, kStageMerge = 3 };
 struct StageEvents {
     void *const *events;
     hipStream_t stream;
     StageEvents(void *const *e, hipStream_t s) : events(e), stream(s) {}
-    hipError_t record(int k) const {
-        return events ? hipEventRecord((hipEvent_t)events[k], stream) : hipSuccess;
+    hipEvent_t start(int stage) const { return events ? (hipEvent_t)events[2 * stage] : nullptr; }
+    hipEvent_t stop(int stage) const { return events ? (hipEvent_t)events[2 * stage + 1] : nullptr; }
+    hipError_t empty(int stage) const {
+        if (!events) return hipSuccess;
+        hipError_t e = hipEventRecord(start(stage), stream);
+        return e == hipSuccess ? hipEventRecord(stop(stage), stream) : e;
     }
 };
 
@@ -299,7 +308,8 @@ int decode_heads_per_group(int D, int Hkv, long long blocks, int nd);
 // not null) receives the count that puts one on every compute unit's
 // resident slots, cus (if not null) the device's compute units.
 hipError_t decode_workgroups(const Params &p, const Plan &plan, int whole, int *nwg, int *fill, int *cus);
-// Launches the decode kernel, records event 3, launches the merge kernel.
+// Launches the decode kernel and the merge kernel (stages kStageDecode and
+// kStageMerge of ev).
 hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stream,
                          const StageEvents &ev);
 // items: the plan kernel's list, or null when the kernel finds its own
@@ -309,8 +319,10 @@ hipError_t launch_decode(const Params &p, const DecodeWork &dw, hipStream_t stre
 // spread: one workgroup per item (a mixed batch's prefill kernel beside the
 // decode kernel); else, up to head_dim 128, one workgroup per compute unit
 // that loops over its items.
+// ev_start / ev_stop (may be null): events given to the kernel launch.
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
-                          const int32_t *counts, bool spread, hipStream_t stream);
+                          const int32_t *counts, bool spread, hipStream_t stream,
+                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 bool prefill_supports(int D, int G);
 // Query rows (heads x tokens) of one prefill workgroup for this head_dim.
 int prefill_rows(int D);

@@ -976,7 +976,8 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(Params p, const int4
 
 template <int D>
 hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
-                            const int32_t *counts, bool spread, hipStream_t stream) {
+                            const int32_t *counts, bool spread, hipStream_t stream, hipEvent_t ev_start,
+                            hipEvent_t ev_stop) {
     // One workgroup per compute unit (LDS holds one), looping over the items,
     // up to head_dim 128 unless spread; else one workgroup per item (with
     // planning on the device, per bound item: those past the count exit).
@@ -1021,14 +1022,14 @@ hipError_t launch_prefill_d(const Params &p, const Plan &plan, const int4 *items
             const int forced = atoi(env);
             if (forced > 0) cus = std::min(cus, forced);
         }
-        hipLaunchKernelGGL((prefill_pp_kernel<D, D <= 128>), dim3(std::min(std::max(1, cus), n)),
-                           dim3(PingPongCfg<D>::NTHR), 0, stream, p, items, mode, plan.q_tile, counts,
-                           plan.n_prefill_items);
+        e = launch_kernel(prefill_pp_kernel<D, D <= 128>, dim3(std::min(std::max(1, cus), n)),
+                          dim3(PingPongCfg<D>::NTHR), 0, stream, ev_start, ev_stop, p, items, mode, plan.q_tile,
+                          counts, plan.n_prefill_items);
     } else {
-        hipLaunchKernelGGL((prefill_pp_kernel<D, false>), dim3(n), dim3(PingPongCfg<D>::NTHR), 0, stream, p, items,
-                           mode, plan.q_tile, counts, plan.n_prefill_items);
+        e = launch_kernel(prefill_pp_kernel<D, false>, dim3(n), dim3(PingPongCfg<D>::NTHR), 0, stream, ev_start,
+                          ev_stop, p, items, mode, plan.q_tile, counts, plan.n_prefill_items);
     }
-    return hipGetLastError();
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace
@@ -1048,11 +1049,12 @@ int prefill_rows(int D) {
 }
 
 hipError_t launch_prefill(const Params &p, const Plan &plan, const int4 *items, bool self_plan,
-                          const int32_t *counts, bool spread, hipStream_t stream) {
+                          const int32_t *counts, bool spread, hipStream_t stream, hipEvent_t ev_start,
+                          hipEvent_t ev_stop) {
     switch (p.D) {
-        case 64: return launch_prefill_d<64>(p, plan, items, self_plan, counts, spread, stream);
-        case 128: return launch_prefill_d<128>(p, plan, items, self_plan, counts, spread, stream);
-        case 256: return launch_prefill_d<256>(p, plan, items, self_plan, counts, spread, stream);
+        case 64: return launch_prefill_d<64>(p, plan, items, self_plan, counts, spread, stream, ev_start, ev_stop);
+        case 128: return launch_prefill_d<128>(p, plan, items, self_plan, counts, spread, stream, ev_start, ev_stop);
+        case 256: return launch_prefill_d<256>(p, plan, items, self_plan, counts, spread, stream, ev_start, ev_stop);
         default: return hipErrorInvalidValue;
     }
 }
