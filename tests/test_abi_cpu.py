@@ -211,3 +211,23 @@ def test_decode_workspace_does_not_grow_with_context(lib):
     # bounded by the partial slots (2 per workgroup, at most 512 workgroups)
     # plus the small per-request tables
     assert n_short <= 2 * 512 * 32 * (128 + 2) * 4 + 64 * 1024
+
+
+def test_profiled_call_checks_its_events(lib):
+    """ra_forward_profiled takes a start and a stop event per stage (eight);
+    a wrong count or a NULL entry is refused before anything else runs."""
+    b = config("tiny")
+    cu, ctx = b.cu_q_lens.clone(), b.context_lens.clone()
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+
+    def call(events, n):
+        return lib.ra_forward_profiled(ctypes.byref(shape_for(b)), fake, fake, fake, fake, fake, fake, fake,
+                                       fake, fake, P(cu.data_ptr()), P(ctx.data_ptr()), fake, P(0x100000),
+                                       ctypes.c_size_t(1 << 30), None, 0, events, n)
+
+    assert binding.StageTimer.N_EVENTS == 8
+    five = (ctypes.c_void_p * 5)(*([0x2000] * 5))
+    assert call(five, 5) == 2  # RA_E_SHAPE: n_events must be 8
+    eight = (ctypes.c_void_p * 8)(*([0x2000] * 7 + [None]))
+    assert call(eight, 8) == 1  # RA_E_NULL: an event is NULL
