@@ -258,8 +258,12 @@ __device__ __forceinline__ int partial_slot(int hg, int b, int b_first, int nwg)
     return (hg * nwg + b) * 2 + (b == b_first ? 1 : 0);
 }
 
+// Workgroups of up to 4 wavefronts at head_dim up to 128 ask for two
+// wavefronts per SIMD (two or more workgroups per compute unit): the kernel
+// then fits in 256 registers without spilling, where the unconstrained
+// allocation (about 270 with accumulation registers) left one.
 template <int D, int HW, int PF, bool NT>
-__global__ __launch_bounds__(64 * HW) void decode_kernel(Params p, DecodeWork dw) {
+__global__ __launch_bounds__(64 * HW, (D <= 128 && HW <= 4) ? 2 : 1) void decode_kernel(Params p, DecodeWork dw) {
     using C = DecodeCfg<D, HW>;
     constexpr int KS = C::KS, MB = C::MB, CPH = C::CPH, CPR = C::CPR, NTHR = C::NTHR,
                   NC = C::NC, SWM = C::SWM, HEAD = C::HEAD, TENSOR = C::TENSOR,
